@@ -1,0 +1,155 @@
+"""CPU oracle for the fused decode GEMV -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The product path (the HIP library and its
+binding) never imports, loads or calls it, and it shares no code with them.
+
+The arithmetic lives in ``gemv_oracle.c`` (plain C, double precision): decode
+every weight exactly, accumulate the dot product of each row in double with
+the column index ascending, then apply the epilogue as a separate pass.  This
+module only marshals numpy arrays into that library, plus the error metric in
+``compare.py``.  Formats and epilogues are named by strings here and numbered
+by the C file itself.
+
+Sources: "feat(cuda): fuse activations and residual add into mmv f/q
+epilogues" (Summary; What changed) for the product and its tails;
+"ggml-cpu: fuse element-wise epilogues (ADD, MUL, SILU) into
+ggml_compute_forward_mul_mat" (What; Correctness) for the multiply tail and
+for the rule that the fused result equals the separate element-wise pass.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+FORMATS = {"f32": 0, "f16": 1, "bf16": 2, "q8b32": 3, "q4b32": 4}
+ACTS = {"none": 0, "sigmoid": 1, "silu": 2, "silu_mul": 3, "mul": 4, "add": 5}
+
+_LIB = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_fp = ctypes.POINTER(ctypes.c_float)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_double.restype = ctypes.c_double
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_weight_bytes.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+        lib.oracle_weight_bytes.restype = ctypes.c_int64
+        lib.oracle_decode_row.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int64, _dp]
+        lib.oracle_decode_row.restype = ctypes.c_int
+        lib.oracle_gemv_rows.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, _fp,
+                                         ctypes.c_int64, ctypes.c_int64, _dp, _dp, _dp]
+        lib.oracle_gemv_rows.restype = ctypes.c_int
+        lib.oracle_sigmoid.argtypes = [ctypes.c_double]
+        lib.oracle_sigmoid.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_epilogue.argtypes = [ctypes.c_int, ctypes.c_int64, _dp, _fp, _fp, _dp]
+        lib.oracle_epilogue.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(a, typ):
+    return a.ctypes.data_as(typ)
+
+
+def f16_to_double(bits: int) -> float:
+    return _lib().oracle_f16_to_double(int(bits))
+
+
+def bf16_to_double(bits: int) -> float:
+    return _lib().oracle_bf16_to_double(int(bits))
+
+
+def sigmoid(a: float) -> float:
+    return _lib().oracle_sigmoid(float(a))
+
+
+def silu(a: float) -> float:
+    return _lib().oracle_silu(float(a))
+
+
+def weight_bytes(fmt: str, N: int, K: int) -> int:
+    return int(_lib().oracle_weight_bytes(FORMATS[fmt], N, K))
+
+
+def _check_w(fmt, N, K, w):
+    nb = weight_bytes(fmt, N, K)
+    if nb < 0:
+        raise ValueError(f"invalid matrix {fmt} {N}x{K}")
+    w = np.ascontiguousarray(w).view(np.uint8).reshape(-1)
+    if w.size < nb:
+        raise ValueError(f"weight buffer holds {w.size} bytes, {fmt} {N}x{K} needs {nb}")
+    return w
+
+
+def decode(fmt: str, N: int, K: int, w: np.ndarray, rows=None) -> np.ndarray:
+    """Exact values of rows [begin, end) of W as float64 [rows, K]."""
+    w = _check_w(fmt, N, K, w)
+    b, e = (0, N) if rows is None else rows
+    out = np.empty((e - b, K), dtype=np.float64)
+    for i in range(b, e):
+        rc = _lib().oracle_decode_row(FORMATS[fmt], N, K, w.ctypes.data, i, _ptr(out[i - b], _dp))
+        if rc != 0:
+            raise ValueError("oracle_decode_row failed")
+    return out
+
+
+def gemv(fmt: str, N: int, K: int, w: np.ndarray, x: np.ndarray, rows=None):
+    """(acc, absacc) for rows [begin, end): acc_i = sum_j w_ij x_j, absacc_i =
+    sum_j |w_ij x_j|, both float64, accumulated in double with j ascending."""
+    w = _check_w(fmt, N, K, w)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.shape != (K,):
+        raise ValueError("x must hold K float32 values")
+    b, e = (0, N) if rows is None else rows
+    acc = np.empty(e - b, dtype=np.float64)
+    absacc = np.empty(e - b, dtype=np.float64)
+    rowbuf = np.empty(K, dtype=np.float64)
+    rc = _lib().oracle_gemv_rows(FORMATS[fmt], N, K, w.ctypes.data, _ptr(x, _fp), b, e,
+                                 _ptr(acc, _dp), _ptr(absacc, _dp), _ptr(rowbuf, _dp))
+    if rc != 0:
+        raise ValueError("oracle_gemv_rows failed")
+    return acc, absacc
+
+
+def epilogue(act: str, acc: np.ndarray, m=None, r=None) -> np.ndarray:
+    """y = act(acc) as its own pass; m and r are the float32 operands."""
+    acc = np.ascontiguousarray(acc, dtype=np.float64).reshape(-1)
+    n = acc.size
+    mp = rp = None
+    if m is not None:
+        m = np.ascontiguousarray(m, dtype=np.float32).reshape(-1)
+        assert m.size == n
+        mp = _ptr(m, _fp)
+    if r is not None:
+        r = np.ascontiguousarray(r, dtype=np.float32).reshape(-1)
+        assert r.size == n
+        rp = _ptr(r, _fp)
+    y = np.empty(n, dtype=np.float64)
+    rc = _lib().oracle_epilogue(ACTS[act], n, _ptr(acc, _dp), mp, rp, _ptr(y, _dp))
+    if rc != 0:
+        raise ValueError(f"oracle_epilogue failed for act={act}")
+    return y
+
+
+def reference(fmt, N, K, w, x, act, m=None, r=None, rows=None):
+    """Full oracle for one call: (y, acc, absacc) over rows [begin, end);
+    m and r are given for all N rows and sliced here."""
+    b, e = (0, N) if rows is None else rows
+    acc, absacc = gemv(fmt, N, K, w, x, rows=(b, e))
+    ms = None if m is None else np.asarray(m, dtype=np.float32).reshape(-1)[b:e]
+    rs = None if r is None else np.asarray(r, dtype=np.float32).reshape(-1)[b:e]
+    return epilogue(act, acc, ms, rs), acc, absacc

@@ -1,0 +1,82 @@
+"""Error metric for comparing a float32 result g against the oracle's y.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+A plain elementwise relative error |g - y| / |y| is not usable for a dot
+product: an output near zero has an unbounded relative condition number, so
+even an exact-order float32 sum fails it on random data.  The guarded metric
+divides instead by the larger of |y_i| and D_i, the first-order magnitude
+through which rounding in the dot product reaches the output:
+
+    err_i = |g_i - y_i| / max(|y_i|, D_i)
+
+with a = acc_i, A = sum_j |w_ij x_j| (the oracle's absacc), s = sigmoid(a):
+
+    none      D = A
+    sigmoid   D = s (1 - s) A
+    silu      D = |s (1 + a (1 - s))| A          (|silu'(a)| A)
+    silu_mul  D = |m_i| |silu'(a)| A
+    mul       D = |m_i| A
+    add       D = A + |r_i|
+
+Any rounding of the float32 dot product obeys |acc_f32 - acc| <= c u A for a
+modest c, so a correct kernel gives err of order c * 2^-24 whatever the data;
+an indexing or layout mistake gives err of order 1.  The tolerances that gate
+parity are per weight format: 1e-5 (f32), 2e-3 (f16, bf16) and 1e-4 (8-bit
+and 4-bit block formats, whose dequantised values are exact).
+"""
+import numpy as np
+
+TOLERANCE = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "q8b32": 1e-4, "q4b32": 1e-4}
+
+
+def _sigmoid(a):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-a))
+
+
+def error_scale(act, acc, absacc, m=None, r=None):
+    a = np.asarray(acc, dtype=np.float64).reshape(-1)
+    A = np.asarray(absacc, dtype=np.float64).reshape(-1)
+    if act == "none":
+        return A.copy()
+    s = _sigmoid(a)
+    dsilu = np.abs(s * (1.0 + a * (1.0 - s)))
+    if act == "sigmoid":
+        return s * (1.0 - s) * A
+    if act == "silu":
+        return dsilu * A
+    if act == "silu_mul":
+        return np.abs(np.asarray(m, dtype=np.float64).reshape(-1)) * dsilu * A
+    if act == "mul":
+        return np.abs(np.asarray(m, dtype=np.float64).reshape(-1)) * A
+    if act == "add":
+        return A + np.abs(np.asarray(r, dtype=np.float64).reshape(-1))
+    raise ValueError(f"unknown act {act}")
+
+
+def compare(g, y, acc, absacc, act, m=None, r=None):
+    """Return a dict: 'max_err' (guarded, the gate), 'argmax', 'max_plain_rel'
+    and 'normwise' (for information), 'n'."""
+    g = np.asarray(g, dtype=np.float64).reshape(-1)
+    y = np.asarray(y, dtype=np.float64).reshape(-1)
+    if g.shape != y.shape:
+        raise ValueError(f"shape mismatch {g.shape} vs {y.shape}")
+    if g.size == 0:
+        return {"max_err": 0.0, "argmax": -1, "max_plain_rel": 0.0, "normwise": 0.0, "n": 0}
+    D = error_scale(act, acc, absacc, m, r)
+    diff = np.abs(g - y)
+    denom = np.maximum(np.abs(y), D)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(diff == 0.0, 0.0, diff / denom)
+        plain = np.where(diff == 0.0, 0.0, diff / np.abs(y))
+    err = np.where(np.isnan(err), np.inf, err)
+    i = int(np.argmax(err))
+    ymax = float(np.max(np.abs(y)))
+    return {
+        "max_err": float(err[i]),
+        "argmax": i,
+        "max_plain_rel": float(np.max(plain)),
+        "normwise": float(np.max(diff) / ymax) if ymax > 0 else float(np.max(diff)),
+        "n": int(g.size),
+    }

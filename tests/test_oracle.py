@@ -1,0 +1,352 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself
+(library conversions, hand-built byte images, exact rational arithmetic,
+closed forms, textbook identities), chosen so that a plausible mistake
+(a dropped term, a wrong sign, index or nibble order, a transposed operand,
+a wrong plane offset) fails at least one of them."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle.compare import TOLERANCE, compare, error_scale
+from decode_gemv_elementwise_amd import synth
+
+U = 2.0 ** -53
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+# ----------------------------------------------------------------- decoders
+
+def test_f16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode("f16", 1, 65536, bits.view(np.uint8))[0]
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # signed zeros keep their sign
+    assert math.copysign(1.0, got[0x8000]) == -1.0
+
+
+def test_bf16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode("bf16", 1, 65536, bits.view(np.uint8))[0]
+    want = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_f32_decode_matches_numpy():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2 ** 32, size=4096, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = np.where(np.isnan(f), np.float32(1.5), f).astype(np.float32)
+    got = oracle.decode("f32", 4, 1024, f.view(np.uint8)).reshape(-1)
+    assert np.array_equal(got, f.astype(np.float64))
+
+
+def _image(fixture):
+    buf = np.zeros(fixture["nbytes"], dtype=np.uint8)
+    for off, hx in fixture["segments"]:
+        b = np.frombuffer(bytes.fromhex(hx), dtype=np.uint8)
+        buf[off:off + b.size] = b
+    return buf
+
+
+@pytest.mark.parametrize("fmt", ["q4b32", "q8b32"])
+def test_block_decode_golden(golden_dir, fmt):
+    fx = json.load(open(os.path.join(golden_dir, f"{fmt}_blocks.json")))
+    N, K = fx["N"], fx["K"]
+    assert oracle.weight_bytes(fmt, N, K) == fx["nbytes"]
+    got = oracle.decode(fmt, N, K, _image(fx))
+    for n, key in enumerate(["expected_row0", "expected_row1"]):
+        want = [Fraction(s) for s in fx[key]]
+        assert [Fraction(v) for v in got[n]] == want, (fmt, n)
+
+
+def test_weight_bytes_spec():
+    assert oracle.weight_bytes("f32", 256, 256) == 262144
+    assert oracle.weight_bytes("f16", 4096, 4096) == 33554432
+    assert oracle.weight_bytes("bf16", 14336, 4096) == 117440512
+    assert oracle.weight_bytes("q8b32", 4096, 6144) == 26738688   # 25165824 codes + 1572864 scales
+    assert oracle.weight_bytes("q4b32", 4096, 14336) == 33030144  # 29360128 nibbles + 3670016 scales
+    assert oracle.weight_bytes("q4b32", 3, 32) == 256 + 6         # 48 code bytes padded to 256
+    assert oracle.weight_bytes("q8b32", 3, 32) == 256 + 6
+    assert oracle.weight_bytes("q4b32", 4, 33) == -1
+    assert oracle.weight_bytes("f32", 0, 4) == -1
+    assert oracle.weight_bytes("f16", 4, 0) == -1
+
+
+@pytest.mark.parametrize("fmt", ["q4b32", "q8b32"])
+def test_pack_decode_roundtrip(fmt):
+    """Packed codes + scales decode to code * scale exactly (code - 8 for 4-bit),
+    with the scale read by numpy's binary16 conversion."""
+    rng = np.random.default_rng(7)
+    N, K = 5, 96
+    w = synth.random_weights(rng, fmt, N, K)
+    got = oracle.decode(fmt, N, K, w.data)
+    codes = w.codes.astype(np.float64) - (8.0 if fmt == "q4b32" else 0.0)
+    want = codes * np.repeat(w.scales.astype(np.float64), 32, axis=1)
+    assert np.array_equal(got, want)
+    assert w.data.size == oracle.weight_bytes(fmt, N, K)
+
+
+# ----------------------------------------------------------------- GEMV
+
+def _exact_values(w: synth.Weights):
+    """Exact weight values as Fractions, decoded independently of the oracle."""
+    N, K = w.N, w.K
+    if w.fmt == "f32":
+        v = w.data.view(np.float32).reshape(N, K).astype(np.float64)
+    elif w.fmt == "f16":
+        v = w.data.view(np.float16).reshape(N, K).astype(np.float64)
+    elif w.fmt == "bf16":
+        t = torch.from_numpy(w.data.view(np.int16).copy()).view(torch.bfloat16)
+        v = t.to(torch.float64).numpy().reshape(N, K)
+    else:
+        off = 8 if w.fmt == "q4b32" else 0
+        return [[Fraction(int(w.codes[i, j]) - off) * Fraction(float(w.scales[i, j // 32]))
+                 for j in range(K)] for i in range(N)]
+    return [[Fraction(float(v[i, j])) for j in range(K)] for i in range(N)]
+
+
+@pytest.mark.parametrize("fmt,N,K", [("f32", 1, 1), ("f32", 3, 7), ("f32", 6, 16), ("f16", 4, 13),
+                                     ("bf16", 5, 11), ("q8b32", 3, 32), ("q8b32", 2, 64),
+                                     ("q4b32", 4, 32), ("q4b32", 3, 64)])
+def test_gemv_brute_force_exact(fmt, N, K):
+    """Against exact rational arithmetic: |acc - exact| <= gamma_{K-1} A and the
+    same for A itself (recursive summation bound)."""
+    rng = np.random.default_rng(N * 1000 + K)
+    w = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    acc, absacc = oracle.gemv(fmt, N, K, w.data, x)
+    ex = _exact_values(w)
+    xf = [Fraction(float(v)) for v in x]
+    for i in range(N):
+        exact = sum(ex[i][j] * xf[j] for j in range(K))
+        A = sum(abs(ex[i][j] * xf[j]) for j in range(K))
+        bound = gamma(max(K - 1, 0)) * float(A)
+        assert abs(float(Fraction(acc[i]) - exact)) <= bound * (1 + 1e-12) + 1e-300
+        assert abs(float(Fraction(absacc[i]) - A)) <= bound * (1 + 1e-12) + 1e-300
+        # all products are exact in double, so fsum gives the correctly rounded sum
+        prods = [float(ex[i][j] * xf[j]) for j in range(K)]
+        assert abs(acc[i] - math.fsum(prods)) <= bound * (1 + 1e-12) + 1e-300
+
+
+def test_gemv_integer_exact():
+    """8-bit blocks with scale 1 and small integer x: every partial sum is an
+    integer below 2^24, so the result is exact and unique."""
+    rng = np.random.default_rng(3)
+    N, K = 8, 6144
+    codes = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    scales = np.ones((N, K // 32), dtype=np.float16)
+    w = synth.pack_q8b32(codes, scales)
+    xi = rng.integers(-3, 4, size=K)
+    acc, absacc = oracle.gemv("q8b32", N, K, w, xi.astype(np.float32))
+    want = codes.astype(np.int64) @ xi
+    wantA = np.abs(codes.astype(np.int64)) @ np.abs(xi)
+    assert np.array_equal(acc, want.astype(np.float64))
+    assert np.array_equal(absacc, wantA.astype(np.float64))
+
+
+def test_gemv_zero_weights():
+    N, K = 7, 33
+    x = synth.draw_vec(np.random.default_rng(0), K)
+    acc, absacc = oracle.gemv("f32", N, K, np.zeros(N * K, dtype=np.float32).view(np.uint8), x)
+    assert np.all(acc == 0) and np.all(absacc == 0)
+
+
+def test_gemv_identity_q4():
+    """4-bit identity: code 9 (value +1 at scale 1) on the diagonal, code 8 (value 0) elsewhere."""
+    N = K = 64
+    codes = np.full((N, K), 8, dtype=np.uint8)
+    np.fill_diagonal(codes, 9)
+    w = synth.pack_q4b32(codes, np.ones((N, K // 32), dtype=np.float16))
+    x = synth.draw_vec(np.random.default_rng(5), K)
+    acc, _ = oracle.gemv("q4b32", N, K, w, x)
+    assert np.array_equal(acc, x.astype(np.float64))
+
+
+def test_gemv_permutation_f16():
+    N = K = 40
+    perm = np.random.default_rng(11).permutation(K)
+    W = np.zeros((N, K), dtype=np.float16)
+    W[np.arange(N), perm] = 1.0
+    x = synth.draw_vec(np.random.default_rng(12), K)
+    acc, _ = oracle.gemv("f16", N, K, W.view(np.uint8), x)
+    assert np.array_equal(acc, x[perm].astype(np.float64))
+
+
+def test_gemv_rank1_nonsquare():
+    """W = u v^T with dyadic entries (every sum exact): acc = u (v . x).  N != K
+    so a transposed operand cannot pass."""
+    rng = np.random.default_rng(13)
+    N, K = 5, 12
+    u = rng.choice([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0], size=N)
+    v = rng.choice([-1.0, -0.25, 0.25, 0.5, 1.0, 3.0], size=K)
+    x = rng.choice([-2.0, -1.0, 0.0, 1.0, 4.0], size=K).astype(np.float32)
+    W = np.outer(u, v).astype(np.float32)
+    acc, _ = oracle.gemv("f32", N, K, W.view(np.uint8), x)
+    assert np.array_equal(acc, u * float(v @ x.astype(np.float64)))
+
+
+def test_gemv_row_slices_match_full():
+    rng = np.random.default_rng(17)
+    w = synth.random_weights(rng, "q4b32", 50, 64)
+    x = synth.draw_vec(rng, 64)
+    acc, absacc = oracle.gemv("q4b32", 50, 64, w.data, x)
+    a2, b2 = oracle.gemv("q4b32", 50, 64, w.data, x, rows=(13, 29))
+    assert np.array_equal(acc[13:29], a2) and np.array_equal(absacc[13:29], b2)
+
+
+# ----------------------------------------------------------------- epilogues
+
+def test_epilogue_closed_forms():
+    ln3 = math.log(3.0)
+    assert oracle.sigmoid(ln3) == pytest.approx(0.75, rel=4e-16)
+    assert oracle.sigmoid(-ln3) == pytest.approx(0.25, rel=4e-16)
+    assert oracle.silu(ln3) == pytest.approx(0.75 * ln3, rel=4e-16)
+    assert oracle.sigmoid(0.0) == 0.5
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.sigmoid(-800.0) == 0.0 and oracle.sigmoid(800.0) == 1.0
+
+
+def test_epilogue_against_library_logistic():
+    a = np.random.default_rng(19).normal(0, 4, size=2000)
+    s = scipy.special.expit(a)
+    y_sig = oracle.epilogue("sigmoid", a)
+    y_silu = oracle.epilogue("silu", a)
+    assert np.allclose(y_sig, s, rtol=4e-16, atol=0)
+    assert np.allclose(y_silu, a * s, rtol=6e-16, atol=0)
+    # identities: sigma(a) + sigma(-a) = 1, silu(a) - silu(-a) = a
+    assert np.allclose(y_sig + oracle.epilogue("sigmoid", -a), 1.0, rtol=0, atol=4e-16)
+    assert np.allclose(y_silu - oracle.epilogue("silu", -a), a, rtol=1e-15, atol=1e-300)
+
+
+def test_epilogue_operands():
+    rng = np.random.default_rng(23)
+    a = rng.normal(size=300)
+    m = synth.draw_vec(rng, 300)
+    r = synth.draw_vec(rng, 300)
+    s = scipy.special.expit(a)
+    assert np.allclose(oracle.epilogue("silu_mul", a, m=m), a * s * m.astype(np.float64), rtol=1e-15, atol=0)
+    assert np.array_equal(oracle.epilogue("mul", a, m=m), a * m.astype(np.float64))
+    assert np.array_equal(oracle.epilogue("add", a, r=r), a + r.astype(np.float64))
+    ones = np.ones(300, dtype=np.float32)
+    zeros = np.zeros(300, dtype=np.float32)
+    assert np.array_equal(oracle.epilogue("silu_mul", a, m=ones), oracle.epilogue("silu", a))
+    assert np.array_equal(oracle.epilogue("mul", a, m=ones), oracle.epilogue("none", a))
+    assert np.array_equal(oracle.epilogue("add", a, r=zeros), oracle.epilogue("none", a))
+    with pytest.raises(ValueError):
+        oracle.epilogue("add", a)
+    with pytest.raises(ValueError):
+        oracle.epilogue("mul", a)
+
+
+def test_zero_w_epilogues():
+    N, K = 16, 32
+    x = synth.draw_vec(np.random.default_rng(29), K)
+    m = synth.draw_vec(np.random.default_rng(30), N)
+    r = synth.draw_vec(np.random.default_rng(31), N)
+    w = np.zeros(N * K, dtype=np.float16).view(np.uint8)
+    want = {"none": 0.0, "sigmoid": 0.5, "silu": 0.0, "silu_mul": 0.0, "mul": 0.0}
+    for act, v in want.items():
+        y, _, _ = oracle.reference("f16", N, K, w, x, act, m=m, r=r)
+        assert np.all(y == v), act
+    y, _, _ = oracle.reference("f16", N, K, w, x, "add", r=r)
+    assert np.array_equal(y, r.astype(np.float64))
+
+
+def test_identity_w_epilogues():
+    """Identity W gives epilogue(x), with the logistic taken from scipy."""
+    N = K = 64
+    codes = np.full((N, K), 8, dtype=np.uint8)
+    np.fill_diagonal(codes, 9)
+    w = synth.pack_q4b32(codes, np.ones((N, K // 32), dtype=np.float16))
+    rng = np.random.default_rng(37)
+    x = synth.draw_vec(rng, K)
+    m = synth.draw_vec(rng, N)
+    xd = x.astype(np.float64)
+    s = scipy.special.expit(xd)
+    y, _, _ = oracle.reference("q4b32", N, K, w, x, "sigmoid")
+    assert np.allclose(y, s, rtol=4e-16, atol=0)
+    y, _, _ = oracle.reference("q4b32", N, K, w, x, "silu_mul", m=m)
+    assert np.allclose(y, xd * s * m, rtol=1e-15, atol=0)
+
+
+# ----------------------------------------------------------------- metric
+
+def test_metric_zero_for_exact_and_scaled_for_perturbation():
+    rng = np.random.default_rng(41)
+    acc = rng.normal(size=100)
+    absacc = np.abs(acc) + rng.uniform(1, 2, size=100)
+    res = compare(acc, acc, acc, absacc, "none")
+    assert res["max_err"] == 0.0
+    g = acc + 1e-5 * absacc
+    assert compare(g, acc, acc, absacc, "none")["max_err"] == pytest.approx(1e-5, rel=1e-9)
+    # near-zero outputs are judged against D, not |y|
+    y0 = np.zeros(4)
+    res = compare(np.full(4, 3e-6), y0, y0, np.full(4, 1.0), "none")
+    assert res["max_err"] == pytest.approx(3e-6) and res["max_plain_rel"] == np.inf
+
+
+def test_metric_error_scales():
+    a = np.array([0.0, 2.0, -3.0])
+    A = np.array([1.0, 2.0, 4.0])
+    m = np.array([2.0, -1.0, 0.5], dtype=np.float32)
+    r = np.array([-1.0, 0.0, 3.0], dtype=np.float32)
+    s = scipy.special.expit(a)
+    ds = s * (1 + a * (1 - s))
+    assert np.allclose(error_scale("sigmoid", a, A), s * (1 - s) * A)
+    assert np.allclose(error_scale("silu", a, A), np.abs(ds) * A)
+    assert np.allclose(error_scale("silu_mul", a, A, m=m), np.abs(m) * np.abs(ds) * A)
+    assert np.allclose(error_scale("mul", a, A, m=m), np.abs(m) * A)
+    assert np.allclose(error_scale("add", a, A, r=r), A + np.abs(r))
+    assert error_scale("silu", np.array([0.0]), np.array([1.0]))[0] == 0.5  # silu'(0) = 1/2
+
+
+def test_float32_rounding_of_oracle_passes_metric():
+    """The oracle's own result rounded to float32 sits far inside every tolerance."""
+    for wl in (synth.f32_tiny_256(0),):
+        for c in wl.calls:
+            w = wl.weights[c.w]
+            m = wl.vectors.get(c.m) if c.m else None
+            r = wl.vectors.get(c.r) if c.r else None
+            y, acc, absacc = oracle.reference(w.fmt, w.N, w.K, w.data, wl.vectors[c.x], c.act, m=m, r=r)
+            res = compare(y.astype(np.float32), y, acc, absacc, c.act, m=m, r=r)
+            assert res["max_err"] < TOLERANCE[w.fmt] * 1e-1
+
+
+# ----------------------------------------------------------------- planted mistakes
+
+def test_pins_catch_planted_mistakes(golden_dir):
+    """Plant plausible mistakes in the oracle's outputs on the CPU and show that
+    the pins above would reject them."""
+    fx = json.load(open(os.path.join(golden_dir, "q4b32_blocks.json")))
+    good = oracle.decode("q4b32", 2, 64, _image(fx))
+    want0 = np.array([float(Fraction(s)) for s in fx["expected_row0"]])
+    assert np.array_equal(good[0], want0)
+    swapped = good[0].reshape(-1, 2)[:, ::-1].reshape(-1)          # nibble order swapped
+    assert not np.array_equal(swapped, want0)
+    no_offset = good[0] + 8.0                                       # dropped the -8
+    assert not np.array_equal(no_offset, want0)
+    # wrong sigmoid sign: 1/(1+exp(a)) fails the closed form sigma(ln 3) = 3/4
+    assert abs(1.0 / (1.0 + math.exp(math.log(3.0))) - 0.75) > 0.1
+    # transposed operand fails the non-square rank-1 pin (shape alone differs)
+    rng = np.random.default_rng(43)
+    W = rng.normal(size=(5, 12)).astype(np.float32)
+    x = rng.normal(size=12).astype(np.float32)
+    acc, _ = oracle.gemv("f32", 5, 12, W.view(np.uint8), x)
+    with pytest.raises(ValueError):
+        oracle.gemv("f32", 12, 5, W.T.copy().view(np.uint8), x)
+    assert acc.shape == (5,)
