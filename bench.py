@@ -1,0 +1,371 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused-epilogue decode GEMV on one MI355X.
+
+A step is one pass of the whole path over one synthetic input: one
+gemv_fused call (validate + launch, x staged into LDS, W streamed from HBM,
+dequantised in registers, dot product, wave reduction, epilogue, store); for
+the 4-bit layer workload, the six calls of the layer.  Inputs are resident in
+HBM before timing starts.  W (and x, operands, dst) rotate over enough copies
+to exceed 512 MiB, so the 256 MB Infinity Cache cannot serve W from a
+previous step.  The timed steps are captured in one HIP graph and replayed
+between two HIP events recorded on the launch stream.
+
+value = algorithmic bytes per step x steps / time, in GB/s, where algorithmic
+bytes = W in its storage format + 4K (x) + 4N per epilogue operand read + 4N
+(dst).  One JSON line on stdout.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "fused GEMV achieved HBM GB/s (% of peak) and µs/call at decode shapes"
+PEAK_HBM_GBPS = 8000.0
+ROTATE_MIN_BYTES = 512 << 20
+DEFAULT_WORKLOAD = "f16_outproj_residual_4096"
+KERNEL_SOURCE = os.path.join(ROOT, "decode_gemv_elementwise_amd", "csrc", "gemv_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                   help="a workload name, or 'all' (one JSON line each)")
+    p.add_argument("--launch", choices=["graph", "stream"], default="graph")
+    p.add_argument("--unfused", action="store_true",
+                   help="time gemv_fused(none) + gemv_epilogue instead of the fused call")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU-oracle sample length (0 disables the cpu_baseline leg)")
+    p.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ setup
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def align(v, a=256):
+    return (v + a - 1) // a * a
+
+
+class Step:
+    """Device copies of one workload, R rotating sets, and the prepared calls
+    of every set (fused, or the unfused composition)."""
+
+    def __init__(self, torch, binding, wl, unfused: bool):
+        self.wl = wl
+        self.calls = wl.calls
+        per_set = sum(w.data.size for w in wl.weights.values())
+        self.copies = max(2, -(-ROTATE_MIN_BYTES // per_set))
+        R = self.copies
+        dev = "cuda"
+        # one allocation per tensor kind, each set at a 256-byte aligned offset
+        self.w_slot = {k: align(w.data.size) for k, w in wl.weights.items()}
+        self.w_buf = {}
+        for k, w in wl.weights.items():
+            buf = torch.empty(R * self.w_slot[k], dtype=torch.uint8, device=dev)
+            src = torch.from_numpy(w.data).to(dev)
+            for i in range(R):
+                buf[i * self.w_slot[k]: i * self.w_slot[k] + w.data.size].copy_(src)
+            self.w_buf[k] = buf
+        self.v_buf = {}
+        for k, v in wl.vectors.items():
+            t = torch.from_numpy(np.ascontiguousarray(v).reshape(-1)).to(dev)
+            self.v_buf[k] = torch.stack([t.clone() for _ in range(R)])
+        self.out_buf = {c.name: torch.zeros((R, wl.weights[c.w].N), dtype=torch.float32, device=dev)
+                        for c in self.calls}
+        self.tmp_buf = {c.name: torch.zeros((R, wl.weights[c.w].N), dtype=torch.float32, device=dev)
+                        for c in self.calls}
+        self.prepared = []
+        for i in range(R):
+            self.prepared.append(self._prepare_set(binding, i, unfused))
+        self.bytes_per_step = sum(self.call_bytes(c) for c in self.calls)
+
+    def _vec(self, name, i, shape=None):
+        if name is None:
+            return None
+        if name.startswith("@"):
+            t = self.out_buf[name[1:]][i]
+        else:
+            t = self.v_buf[name][i]
+        return t.view(shape) if shape else t
+
+    def _prepare_set(self, binding, i, unfused):
+        fns = []
+        for c in self.calls:
+            w = self.wl.weights[c.w]
+            W = self.w_buf[c.w][i * self.w_slot[c.w]:]
+            x = self._vec(c.x, i)
+            shape = c.out_shape or (w.N,)
+            m = self._vec(c.m, i, shape)
+            r = self._vec(c.r, i, shape)
+            if c.inplace:
+                dst = r if c.act == "add" else m
+            else:
+                dst = self.out_buf[c.name][i].view(shape)
+            if unfused and c.act != "none":
+                tmp = self.tmp_buf[c.name][i]
+                fns.append(binding.PreparedCall(W, w.fmt, w.N, w.K, x, "none", dst=tmp))
+                fns.append(_PreparedEpilogue(binding, c.act, w.N, tmp, m, r, dst))
+            else:
+                fns.append(binding.PreparedCall(W, w.fmt, w.N, w.K, x, c.act, mul_operand=m, add_operand=r,
+                                                dst=dst))
+        return fns
+
+    def call_bytes(self, c):
+        w = self.wl.weights[c.w]
+        ops = (1 if c.m else 0) + (1 if c.r else 0)
+        return w.data.size + 4 * w.K + 4 * w.N * ops + 4 * w.N
+
+    def launches_per_step(self):
+        return len(self.prepared[0])
+
+
+class _PreparedEpilogue:
+    def __init__(self, binding, act, N, acc, m, r, dst):
+        self.args = (act, N, acc, m, r, dst)
+        self.binding = binding
+
+    def __call__(self):
+        act, N, acc, m, r, dst = self.args
+        self.binding.gemv_epilogue(act, N, acc, mul_operand=m, add_operand=r, dst=dst)
+
+
+def run_steps(step, n, offset=0):
+    R = step.copies
+    for s in range(n):
+        for fn in step.prepared[(offset + s) % R]:
+            fn()
+
+
+def time_steps(torch, step, steps, warmup, launch):
+    """Returns elapsed seconds for `steps` steps after `warmup` untimed ones,
+    measured with HIP events on the stream the kernels are launched on."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        run_steps(step, 1)  # first launch outside any capture
+        torch.cuda.synchronize()
+        if launch == "graph":
+            gw = torch.cuda.CUDAGraph() if warmup > 0 else None
+            if gw is not None:
+                with torch.cuda.graph(gw, stream=stream):
+                    run_steps(step, warmup)
+            gt = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gt, stream=stream):
+                run_steps(step, steps, offset=warmup)
+            torch.cuda.synchronize()
+            if gw is not None:
+                gw.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            gt.replay()
+            e1.record(stream)
+        else:
+            run_steps(step, warmup)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            run_steps(step, steps, offset=warmup)
+            e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3
+
+
+def probe_bandwidth(torch, nbytes=2 << 30):
+    import ctypes
+    from decode_gemv_elementwise_amd import build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    blocks = 2048
+    out = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        assert lib.hbm_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), blocks, s) == 0
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    reps = 10
+    for _ in range(reps):
+        lib.hbm_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), blocks, s)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    ok = float(out.sum()) == nbytes / 4
+    del buf
+    return nbytes / sec / 1e9, ok
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle as written (single thread, double precision), on full calls of
+    the same workload, for about `seconds` of CPU time."""
+    import oracle
+    calls = wl.calls
+    outputs = {}
+    t0 = time.perf_counter()
+    nbytes = 0
+    ncalls = 0
+    while True:
+        for c in calls:
+            w = wl.weights[c.w]
+            x = outputs[c.x[1:]] if c.x.startswith("@") else wl.vectors[c.x]
+            m = (outputs[c.m[1:]] if c.m.startswith("@") else wl.vectors[c.m]) if c.m else None
+            r = wl.vectors[c.r] if c.r else None
+            y, _, _ = oracle.reference(w.fmt, w.N, w.K, w.data, x, c.act, m=m, r=r)
+            outputs[c.name] = y.astype(np.float32)
+            ops = (1 if c.m else 0) + (1 if c.r else 0)
+            nbytes += w.data.size + 4 * w.K + 4 * w.N * ops + 4 * w.N
+            ncalls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{ncalls} full calls of {wl.name} (every row, double accumulation, "
+                      f"separate epilogue pass) in {el:.1f} s on one host thread",
+            "us_per_call": round(el / ncalls * 1e6, 1)}
+
+
+def read_counters(workload):
+    """Per-launch HBM traffic (bytes) from the committed rocprofv3 counter
+    summary of this workload's dominant kernel, if it was taken on the current
+    kernel source; else None."""
+    path = os.path.join(PROFILES, f"counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_sha():
+        return None
+    try:
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def bench_workload(torch, binding, synth, name, args, probe):
+    wl = synth.WORKLOADS[name](0)
+    log(f"workload {name}: preparing rotating copies")
+    step = Step(torch, binding, wl, args.unfused)
+    log(f"  {step.copies} copies, {step.launches_per_step()} launches/step, "
+        f"{step.bytes_per_step} algorithmic bytes/step")
+    sec = time_steps(torch, step, args.steps, args.warmup, args.launch)
+    ms_per_step = sec / args.steps * 1e3
+    value = step.bytes_per_step * args.steps / sec / 1e9
+
+    # dominant kernel: the call with the most bytes; timed alone the same way
+    dom = max(wl.calls, key=step.call_bytes)
+    if len(wl.calls) == 1 and step.launches_per_step() == 1:
+        dom_sec = sec / args.steps
+    else:
+        # inputs produced by earlier calls of the step become fresh vectors of
+        # the same length (timing only)
+        vecs = dict(wl.vectors)
+        w = wl.weights[dom.w]
+        x, m = dom.x, dom.m
+        if x.startswith("@"):
+            x = "_x_alone"
+            vecs[x] = synth.draw_vec(np.random.default_rng(1), w.K)
+        if m and m.startswith("@"):
+            m = "_m_alone"
+            vecs[m] = synth.draw_vec(np.random.default_rng(2), w.N)
+        alone = synth.Call(dom.name, dom.w, x, dom.act, m=m, r=dom.r, out_shape=dom.out_shape,
+                           inplace=dom.inplace)
+        sub = synth.Workload(wl.name, {dom.w: w}, vecs, [alone])
+        dstep = Step(torch, binding, sub, False)
+        dom_sec = time_steps(torch, dstep, args.steps, args.warmup, args.launch) / args.steps
+        del dstep
+    dom_bytes = step.call_bytes(dom)
+    achieved = dom_bytes / dom_sec / 1e9
+    traffic = read_counters(name)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "calls": [
+            {"name": c.name, "wfmt": wl.weights[c.w].fmt, "N": wl.weights[c.w].N, "K": wl.weights[c.w].K,
+             "epilogue": c.act + (" in place" if c.inplace else "") + (f" view {list(c.out_shape)}"
+                                                                      if c.out_shape else "")}
+            for c in wl.calls],
+            "fused": not args.unfused, "launches_per_step": step.launches_per_step(),
+            "launch": args.launch, "rotating_copies": step.copies,
+            "algorithmic_bytes_per_step": step.bytes_per_step},
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": f"gemv_fast_kernel<{wl.weights[dom.w].fmt}> ({dom.name})",
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "us_per_launch": round(dom_sec * 1e6, 3)},
+    }
+    if probe is not None:
+        res["probe_read_gbps"] = round(probe, 1)
+        res["roofline"]["frac_of_probe"] = round(achieved / probe, 4)
+    del step
+    torch.cuda.empty_cache()
+    return res, wl
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the fused GEMV has no multi-GPU path in this "
+              "library (row or K sharding is described in the design notes); use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("steps must be >= 1 and warmup >= 0")
+    import torch
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    from decode_gemv_elementwise_amd import binding, synth
+    binding.load()  # fails loudly if the HIP library is not built
+
+    probe = None
+    if not args.no_probe:
+        probe, ok = probe_bandwidth(torch)
+        log(f"read probe: {probe:.1f} GB/s (sum check {'ok' if ok else 'FAILED'})")
+    names = list(synth.WORKLOADS) if args.workload == "all" else [args.workload]
+    for i, name in enumerate(names):
+        res, wl = bench_workload(torch, binding, synth, name, args, probe)
+        if i == 0 and args.cpu_seconds > 0:
+            log("cpu baseline (oracle)")
+            res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

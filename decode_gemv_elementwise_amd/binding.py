@@ -1,0 +1,202 @@
+"""ctypes binding of the C ABI in ``include/gemv_fused.h``.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  Functions carry the C names.  Tensors are torch tensors (device
+memory) or, for the host-only checks, raw integer addresses with explicit
+shapes.  There is no fallback: if ``libgemv_fused.so`` is missing, loading
+fails with an error that says how to build it.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgemv_fused.so")
+
+FORMATS = {"f32": 0, "f16": 1, "bf16": 2, "q8b32": 3, "q4b32": 4}
+ACTS = {"none": 0, "sigmoid": 1, "silu": 2, "silu_mul": 3, "mul": 4, "add": 5}
+STATUS = {0: "GEMV_OK", -1: "GEMV_E_NULL", -2: "GEMV_E_DIM", -3: "GEMV_E_FMT", -4: "GEMV_E_ACT",
+          -5: "GEMV_E_OPERAND", -6: "GEMV_E_LAYOUT", -7: "GEMV_E_ALIAS", -8: "GEMV_E_ALIGN", -9: "GEMV_E_HIP"}
+STATUS_CODE = {v: k for k, v in STATUS.items()}
+MAX_DIMS = 4
+
+
+class GemvView(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * MAX_DIMS), ("stride", ctypes.c_int64 * MAX_DIMS)]
+
+
+class GemvError(RuntimeError):
+    def __init__(self, status, message, hip_error=0):
+        super().__init__(f"{STATUS.get(status, status)}: {message}"
+                         + (f" (hipError {hip_error})" if hip_error else ""))
+        self.status = status
+        self.hip_error = hip_error
+
+
+_LIB = None
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_VIEWP = ctypes.POINTER(GemvView)
+
+
+def load():
+    """Load libgemv_fused.so (build it with ``python -m decode_gemv_elementwise_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_gemv_elementwise_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.gemv_fused.argtypes = [_VP, ctypes.c_int, _I64, _I64, _VP, ctypes.c_int, _VIEWP, _VIEWP, _VIEWP, _VP]
+    lib.gemv_fused.restype = ctypes.c_int
+    lib.gemv_validate.argtypes = [_VP, ctypes.c_int, _I64, _I64, _VP, ctypes.c_int, _VIEWP, _VIEWP, _VIEWP]
+    lib.gemv_validate.restype = ctypes.c_int
+    lib.gemv_epilogue.argtypes = [ctypes.c_int, _I64, _VP, _VIEWP, _VIEWP, _VIEWP, _VP]
+    lib.gemv_epilogue.restype = ctypes.c_int
+    lib.gemv_epilogue_validate.argtypes = [ctypes.c_int, _I64, _VP, _VIEWP, _VIEWP, _VIEWP]
+    lib.gemv_epilogue_validate.restype = ctypes.c_int
+    lib.gemv_weight_bytes.argtypes = [ctypes.c_int, _I64, _I64]
+    lib.gemv_weight_bytes.restype = _I64
+    lib.gemv_strerror.argtypes = [ctypes.c_int]
+    lib.gemv_strerror.restype = ctypes.c_char_p
+    lib.gemv_last_hip_error.argtypes = []
+    lib.gemv_last_hip_error.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _addr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def make_view(data, shape=None, stride=None) -> GemvView:
+    """A GemvView from a torch tensor (f32), or from an address plus shape and
+    strides (in elements; C-contiguous strides by default)."""
+    if not isinstance(data, int):
+        import torch
+        if data.dtype != torch.float32:
+            raise TypeError("epilogue operands and dst are float32")
+        shape = tuple(data.shape) if shape is None else tuple(shape)
+        stride = tuple(data.stride()) if stride is None else tuple(stride)
+        if len(shape) == 0:
+            shape, stride = (1,), (1,)
+        data = data.data_ptr()
+    shape = tuple(shape)
+    if stride is None:
+        st, acc = [], 1
+        for s in reversed(shape):
+            st.append(acc)
+            acc *= s
+        stride = tuple(reversed(st))
+    if not 1 <= len(shape) <= MAX_DIMS or len(stride) != len(shape):
+        # pass the rank through unchanged so the library reports the layout error
+        v = GemvView()
+        v.data = data
+        v.ndim = len(shape)
+        for i, (s, t) in enumerate(list(zip(shape, stride))[:MAX_DIMS]):
+            v.shape[i], v.stride[i] = s, t
+        return v
+    v = GemvView()
+    v.data = data
+    v.ndim = len(shape)
+    for i, (s, t) in enumerate(zip(shape, stride)):
+        v.shape[i] = s
+        v.stride[i] = t
+    return v
+
+
+def _as_view(v):
+    if v is None:
+        return None
+    if isinstance(v, GemvView):
+        return ctypes.pointer(v)
+    return ctypes.pointer(make_view(v))
+
+
+def _fmt(wfmt):
+    return FORMATS[wfmt] if isinstance(wfmt, str) else int(wfmt)
+
+
+def _act(act):
+    return ACTS[act] if isinstance(act, str) else int(act)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _raise(status):
+    lib = load()
+    raise GemvError(status, lib.gemv_strerror(status).decode(),
+                    lib.gemv_last_hip_error() if status == STATUS_CODE["GEMV_E_HIP"] else 0)
+
+
+# ------------------------------------------------------------------ API (C names)
+
+def gemv_fused(W, wfmt, N, K, x, act, mul_operand=None, add_operand=None, dst=None, stream=None):
+    """dst = epilogue(W x) on the GPU (one launch, asynchronous on ``stream``;
+    default: torch's current stream).  Raises GemvError on a rejected call."""
+    st = load().gemv_fused(_addr(W), _fmt(wfmt), N, K, _addr(x), _act(act), _as_view(mul_operand),
+                           _as_view(add_operand), _as_view(dst), _stream(stream))
+    if st != 0:
+        _raise(st)
+
+
+def gemv_validate(W, wfmt, N, K, x, act, mul_operand=None, add_operand=None, dst=None) -> int:
+    """Host-only checks; returns the status code (no HIP call)."""
+    return load().gemv_validate(_addr(W), _fmt(wfmt), N, K, _addr(x), _act(act), _as_view(mul_operand),
+                                _as_view(add_operand), _as_view(dst))
+
+
+def gemv_epilogue(act, N, acc, mul_operand=None, add_operand=None, dst=None, stream=None):
+    """dst = epilogue(acc) as a separate pass (the unfused path)."""
+    st = load().gemv_epilogue(_act(act), N, _addr(acc), _as_view(mul_operand), _as_view(add_operand),
+                              _as_view(dst), _stream(stream))
+    if st != 0:
+        _raise(st)
+
+
+def gemv_epilogue_validate(act, N, acc, mul_operand=None, add_operand=None, dst=None) -> int:
+    return load().gemv_epilogue_validate(_act(act), N, _addr(acc), _as_view(mul_operand),
+                                         _as_view(add_operand), _as_view(dst))
+
+
+def gemv_weight_bytes(wfmt, N, K) -> int:
+    return int(load().gemv_weight_bytes(_fmt(wfmt), N, K))
+
+
+def gemv_strerror(status: int) -> str:
+    return load().gemv_strerror(status).decode()
+
+
+def gemv_last_hip_error() -> int:
+    return int(load().gemv_last_hip_error())
+
+
+class PreparedCall:
+    """A gemv_fused call with its views marshalled once, for tight loops and
+    graph capture (the tensors must stay alive and in place)."""
+
+    def __init__(self, W, wfmt, N, K, x, act, mul_operand=None, add_operand=None, dst=None):
+        self._lib = load()
+        self._views = [None if v is None else (v if isinstance(v, GemvView) else make_view(v))
+                       for v in (mul_operand, add_operand, dst)]
+        self._ptrs = [None if v is None else ctypes.pointer(v) for v in self._views]
+        self._args = (_addr(W), _fmt(wfmt), N, K, _addr(x), _act(act))
+
+    def __call__(self, stream=None):
+        st = self._lib.gemv_fused(*self._args, *self._ptrs, _stream(stream))
+        if st != 0:
+            _raise(st)

@@ -1,0 +1,20 @@
+// Internal declarations shared by the host checks (gemv_validate.cpp) and the
+// HIP translation unit (gemv_kernels.hip).  Host code only.
+#pragma once
+
+#include <cstdint>
+
+#include "gemv_fused.h"
+
+namespace gemv {
+
+inline int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+int64_t weight_bytes(int wfmt, int64_t N, int64_t K);
+int validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int act,
+             const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst);
+int validate_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul_operand,
+                      const gemv_view *add_operand, const gemv_view *dst);
+const char *strerror_of(int status);
+
+} // namespace gemv

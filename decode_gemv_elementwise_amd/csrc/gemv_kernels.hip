@@ -1,0 +1,515 @@
+// Fused-epilogue decode GEMV for CDNA4 (gfx950): dst = epilogue(W x), one
+// output column, one launch per call.
+//
+// What is computed follows "feat(cuda): fuse activations and residual add
+// into mmv f/q epilogues" ("Summary", "What changed"): the matrix-vector
+// product of the decode path with a run-time epilogue (none, sigmoid, silu,
+// silu times a per-row operand, a residual add, possibly through a reshape of
+// the output) applied to the accumulator before the one store; and "ggml-cpu:
+// fuse element-wise epilogues (ADD, MUL, SILU) into
+// ggml_compute_forward_mul_mat" ("What") for the plain multiply tail.  The
+// kernel design is this library's own, for gfx950:
+//
+//  * x is staged once per workgroup into LDS, as f32, laid out in 16-byte
+//    W-chunk order with 4 floats of padding after every chunk of 8+ floats,
+//    so that the 16-byte LDS reads of consecutive lanes (consecutive chunks)
+//    fall in distinct banks.
+//  * Each wave streams R rows at a time: lane l loads 16-byte chunks
+//    l, l + 64, ... of each row with nontemporal 128-bit loads (a wave's load
+//    instruction covers 1 KiB of one row), reads the matching x values from
+//    LDS once and uses them for all R rows.
+//  * Register-level dequantisation: f16 and 4-bit codes become packed f16
+//    pairs consumed by mixed-precision FMAs (f16 x f32 + f32); bf16 is a
+//    shift; 8-bit codes a sign-extending convert.  All products are formed
+//    exactly inside the FMA; only the f32 sums round.
+//  * The 64 lane partials of a row are reduced with DPP row operations and
+//    four lane reads, in a fixed order: results are deterministic.
+//  * The epilogue is a run-time switch on a uniform value, applied by one lane
+//    per row; the same __device__ function serves the unfused pass, so fused
+//    and unfused results are identical for the same accumulator.
+//
+// No MFMA: one column is not a dense contraction, and the kernel is bound by
+// HBM bandwidth (<= 4 flops per weight byte).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <mutex>
+
+#include "gemv_internal.h"
+
+namespace gemv {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+__host__ __device__ __forceinline__ int64_t align256_dev(int64_t v) { return (v + 255) / 256 * 256; }
+constexpr int kMaxLds = 160 * 1024; // LDS bytes a gfx950 workgroup may allocate
+
+// ------------------------------------------------------------------ epilogue
+
+// sigmoid(a) = 1 / (1 + e^-a) and silu(a) = a * sigmoid(a), evaluated with
+// t = e^-|a| <= 1 so that nothing overflows: for a < 0 the same values are
+// t / (1 + t) and a t / (1 + t).  (The direct form turns silu(a) into -0 once
+// e^-a overflows, near a = -88.7, although the true value is still a normal
+// float there.)
+__device__ __forceinline__ float sigmoid_f(float a)
+{
+    float t = expf(-fabsf(a));
+    return (a >= 0.0f ? 1.0f : t) / (1.0f + t);
+}
+
+__device__ __forceinline__ float silu_f(float a)
+{
+    float t = expf(-fabsf(a));
+    return (a >= 0.0f ? a : a * t) / (1.0f + t);
+}
+
+__device__ __forceinline__ float apply_epilogue(int act, float a, const float *m, const float *r, int64_t i)
+{
+    switch (act) {
+    case GEMV_ACT_SIGMOID:
+        return sigmoid_f(a);
+    case GEMV_ACT_SILU:
+        return silu_f(a);
+    case GEMV_ACT_SILU_MUL: {
+        float s = silu_f(a);
+        return s * m[i];
+    }
+    case GEMV_ACT_MUL:
+        return a * m[i];
+    case GEMV_ACT_ADD:
+        return a + r[i];
+    default:
+        return a;
+    }
+}
+
+// ------------------------------------------------------------------ wave reduce
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_read(float v, int l)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Sum of v over the 64 lanes, returned uniformly.  quad_perm swaps, then
+// half-row and row mirrors leave each 16-lane row's sum in all its lanes.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v); // row_half_mirror
+    v += dpp<0x140>(v); // row_mirror
+    return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
+}
+
+// ------------------------------------------------------------------ formats
+// E:   weights per 16-byte chunk of W.
+// XS:  LDS floats per chunk of x (E plus padding).
+// kBlock: the format has an fp16 scale plane; a chunk is 1/kChunksPerBlock
+//         of a 32-weight block.
+
+__device__ __forceinline__ float f16lo(unsigned d) { return (float)__builtin_bit_cast(f16x2, d).x; }
+__device__ __forceinline__ float f16hi(unsigned d) { return (float)__builtin_bit_cast(f16x2, d).y; }
+
+template <int FMT> struct Fmt;
+
+template <> struct Fmt<GEMV_W_F32> {
+    static constexpr int E = 4, XS = 4;
+    static constexpr bool kBlock = false;
+    static constexpr int kChunksPerBlock = 0;
+    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float acc)
+    {
+        // Copy the lanes out before reinterpreting: __builtin_bit_cast applied
+        // to an element of an ext_vector_type reads the vector's first element.
+        unsigned d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = fmaf(__builtin_bit_cast(float, d[i]), xv[i], acc);
+        return acc;
+    }
+};
+
+template <> struct Fmt<GEMV_W_F16> {
+    static constexpr int E = 8, XS = 12;
+    static constexpr bool kBlock = false;
+    static constexpr int kChunksPerBlock = 0;
+    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float acc)
+    {
+        unsigned d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = fmaf(f16lo(d[i]), xv[2 * i], acc);
+            acc = fmaf(f16hi(d[i]), xv[2 * i + 1], acc);
+        }
+        return acc;
+    }
+};
+
+template <> struct Fmt<GEMV_W_BF16> {
+    static constexpr int E = 8, XS = 12;
+    static constexpr bool kBlock = false;
+    static constexpr int kChunksPerBlock = 0;
+    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float acc)
+    {
+        unsigned d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = fmaf(__builtin_bit_cast(float, d[i] << 16), xv[2 * i], acc);
+            acc = fmaf(__builtin_bit_cast(float, d[i] & 0xFFFF0000u), xv[2 * i + 1], acc);
+        }
+        return acc;
+    }
+};
+
+// 8-bit blocks: a chunk is 16 codes (half a block).  Partial sum of code * x,
+// then one multiply-add by the block scale.
+template <> struct Fmt<GEMV_W_Q8B32> {
+    static constexpr int E = 16, XS = 20;
+    static constexpr bool kBlock = true;
+    static constexpr int kChunksPerBlock = 2;
+    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float scale, float acc)
+    {
+        unsigned d[4] = {q.x, q.y, q.z, q.w};
+        float p = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                float w = (float)(int)(signed char)((d[i] >> (8 * b)) & 0xFF);
+                p = fmaf(w, xv[4 * i + b], p);
+            }
+        }
+        return fmaf(p, scale, acc);
+    }
+};
+
+// 4-bit blocks: a chunk is one whole block of 32 codes.  A dword holds
+// elements 8i..8i+7, element k in bits 4k..4k+3.  OR-ing a nibble into the
+// mantissa of the f16 constant 1024 gives 1024 + c exactly (nibble at bit 0)
+// or 1024 + 16c (nibble at bit 4); subtracting 1032 or 1152 leaves c - 8 or
+// 16 (c - 8) exactly, as a packed f16 pair.  The 16x lane is folded back with
+// an exact multiply by 1/16 once per block.
+template <> struct Fmt<GEMV_W_Q4B32> {
+    static constexpr int E = 32, XS = 36;
+    static constexpr bool kBlock = true;
+    static constexpr int kChunksPerBlock = 1;
+    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float scale, float acc)
+    {
+        const f16x2 off1 = {(_Float16)1032.0f, (_Float16)1032.0f};
+        const f16x2 off16 = {(_Float16)1152.0f, (_Float16)1152.0f};
+        unsigned d[4] = {q.x, q.y, q.z, q.w};
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float *xi = xv + 8 * i;
+            unsigned e = d[i] >> 8;
+            f16x2 h0 = __builtin_bit_cast(f16x2, (d[i] & 0x000F000Fu) | 0x64006400u) - off1;  // c0-8, c4-8
+            f16x2 h1 = __builtin_bit_cast(f16x2, (d[i] & 0x00F000F0u) | 0x64006400u) - off16; // 16(c1-8), 16(c5-8)
+            f16x2 h2 = __builtin_bit_cast(f16x2, (e & 0x000F000Fu) | 0x64006400u) - off1;     // c2-8, c6-8
+            f16x2 h3 = __builtin_bit_cast(f16x2, (e & 0x00F000F0u) | 0x64006400u) - off16;    // 16(c3-8), 16(c7-8)
+            a0 = fmaf((float)h0.x, xi[0], a0);
+            a0 = fmaf((float)h0.y, xi[4], a0);
+            a0 = fmaf((float)h2.x, xi[2], a0);
+            a0 = fmaf((float)h2.y, xi[6], a0);
+            a1 = fmaf((float)h1.x, xi[1], a1);
+            a1 = fmaf((float)h1.y, xi[5], a1);
+            a1 = fmaf((float)h3.x, xi[3], a1);
+            a1 = fmaf((float)h3.y, xi[7], a1);
+        }
+        return fmaf(fmaf(a1, 0.0625f, a0), scale, acc);
+    }
+};
+
+// Byte layout helpers (see the header for the formats).
+template <int FMT> __host__ __device__ __forceinline__ int64_t row_bytes(int64_t K)
+{
+    return FMT == GEMV_W_F32 ? K * 4 : (FMT == GEMV_W_Q8B32 ? K : (FMT == GEMV_W_Q4B32 ? K / 2 : K * 2));
+}
+
+__device__ __forceinline__ float load_scale(const unsigned char *p)
+{
+    unsigned short h = *reinterpret_cast<const unsigned short *>(p);
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// ------------------------------------------------------------------ fast kernel
+// Requires: W 16-byte aligned, row_bytes(K) % 16 == 0, (K / E) * XS * 4 bytes
+// of LDS.  Grid: any number of workgroups; each takes tiles of WAVES * R rows
+// in a grid-stride loop.
+
+template <int FMT, int WAVES, int R>
+__global__ __launch_bounds__(WAVES *kWave) void gemv_fast_kernel(const unsigned char *__restrict__ W,
+                                                                 const float *__restrict__ x, int N, int K,
+                                                                 int act, const float *mop, const float *rop,
+                                                                 float *dst)
+{
+    using F = Fmt<FMT>;
+    extern __shared__ f32x4 lds4[];
+    float *xs = reinterpret_cast<float *>(lds4);
+
+    const int nchunks = K / F::E;
+    // Stage x: 4 floats at a time (K % 4 == 0 here), into padded chunk order.
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+        for (int k4 = threadIdx.x; k4 < K / 4; k4 += blockDim.x) {
+            int k = 4 * k4;
+            *reinterpret_cast<f32x4 *>(xs + (k / F::E) * F::XS + (k % F::E)) = x4[k4];
+        }
+    } else {
+        for (int k = threadIdx.x; k < K; k += blockDim.x)
+            xs[(k / F::E) * F::XS + (k % F::E)] = x[k];
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int rows_per_tile = WAVES * R;
+    const int ntiles = (N + rows_per_tile - 1) / rows_per_tile;
+    const int64_t rbytes = row_bytes<FMT>(K);
+    const unsigned char *scales = F::kBlock ? W + align256_dev((int64_t)N * rbytes) : nullptr;
+    const int64_t scales_per_row = K / 32;
+
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int row0 = tile * rows_per_tile + wave * R;
+        const unsigned char *wrow[R];
+        const unsigned char *srow[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int row = min(row0 + r, N - 1);
+            wrow[r] = W + (int64_t)row * rbytes;
+            srow[r] = F::kBlock ? scales + (int64_t)row * scales_per_row * 2 : nullptr;
+        }
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[r] = 0.0f;
+
+        for (int c = lane; c < nchunks; c += kWave) {
+            u32x4 q[R];
+            float sc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[r]) + c);
+                if constexpr (F::kBlock)
+                    sc[r] = load_scale(srow[r] + 2 * (c / F::kChunksPerBlock));
+            }
+            float xv[F::E];
+            const f32x4 *xl = reinterpret_cast<const f32x4 *>(xs + c * F::XS);
+#pragma unroll
+            for (int i = 0; i < F::E / 4; ++i) {
+                f32x4 t = xl[i];
+                xv[4 * i] = t.x;
+                xv[4 * i + 1] = t.y;
+                xv[4 * i + 2] = t.z;
+                xv[4 * i + 3] = t.w;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if constexpr (F::kBlock)
+                    acc[r] = F::dot(q[r], xv, sc[r], acc[r]);
+                else
+                    acc[r] = F::dot(q[r], xv, acc[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float s = wave_sum(acc[r]);
+            int row = row0 + r;
+            if (lane == r && row < N)
+                dst[row] = apply_epilogue(act, s, mop, rop, row);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ generic kernel
+// Any K and alignment (float formats with K not a multiple of the 16-byte
+// chunk, or x too long for LDS): one wave per row, element loads, x read
+// through the caches.
+
+template <int FMT> __device__ __forceinline__ float weight_at(const unsigned char *W, int N, int K, int row, int k)
+{
+    if constexpr (FMT == GEMV_W_F32) {
+        return reinterpret_cast<const float *>(W)[(int64_t)row * K + k];
+    } else if constexpr (FMT == GEMV_W_F16) {
+        return (float)reinterpret_cast<const _Float16 *>(W)[(int64_t)row * K + k];
+    } else if constexpr (FMT == GEMV_W_BF16) {
+        unsigned short b = reinterpret_cast<const unsigned short *>(W)[(int64_t)row * K + k];
+        return __builtin_bit_cast(float, (unsigned)b << 16);
+    } else if constexpr (FMT == GEMV_W_Q8B32) {
+        const unsigned char *scales = W + align256_dev((int64_t)N * K);
+        float s = load_scale(scales + ((int64_t)row * (K / 32) + k / 32) * 2);
+        return (float)(int)(signed char)W[(int64_t)row * K + k] * s;
+    } else {
+        const unsigned char *scales = W + align256_dev((int64_t)N * K / 2);
+        float s = load_scale(scales + ((int64_t)row * (K / 32) + k / 32) * 2);
+        unsigned char b = W[(int64_t)row * (K / 2) + k / 2];
+        int c = (k & 1) ? (b >> 4) : (b & 0xF);
+        return (float)(c - 8) * s;
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void gemv_generic_kernel(const unsigned char *__restrict__ W,
+                                                           const float *__restrict__ x, int N, int K, int act,
+                                                           const float *mop, const float *rop, float *dst)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nwaves = gridDim.x * (blockDim.x / kWave);
+    for (int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; row < N; row += nwaves) {
+        float acc = 0.0f;
+        for (int k = lane; k < K; k += kWave)
+            acc = fmaf(weight_at<FMT>(W, N, K, row, k), x[k], acc);
+        float s = wave_sum(acc);
+        if (lane == 0)
+            dst[row] = apply_epilogue(act, s, mop, rop, row);
+    }
+}
+
+// ------------------------------------------------------------------ unfused epilogue
+
+__global__ __launch_bounds__(256) void gemv_epilogue_kernel(int N, const float *acc, int act, const float *mop,
+                                                            const float *rop, float *dst)
+{
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < N)
+        dst[i] = apply_epilogue(act, acc[i], mop, rop, i);
+}
+
+// ------------------------------------------------------------------ host dispatch
+
+thread_local int t_last_hip_error = 0;
+
+struct Call {
+    const unsigned char *W;
+    const float *x;
+    int N, K, act;
+    const float *m, *r;
+    float *dst;
+};
+
+template <int FMT> constexpr int lds_bytes_fast(int K) { return (K / Fmt<FMT>::E) * Fmt<FMT>::XS * 4; }
+
+template <int FMT, int WAVES, int R> hipError_t launch_fast(const Call &c, hipStream_t s)
+{
+    const void *fn = reinterpret_cast<const void *>(&gemv_fast_kernel<FMT, WAVES, R>);
+    size_t lds = (size_t)lds_bytes_fast<FMT>(c.K);
+    if (lds > 64 * 1024) {
+        static std::once_flag once;
+        static hipError_t attr_err = hipSuccess;
+        std::call_once(once, [&] { attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds); });
+        if (attr_err != hipSuccess)
+            return attr_err;
+    }
+    const int rows_per_tile = WAVES * R;
+    int ntiles = (c.N + rows_per_tile - 1) / rows_per_tile;
+    int grid = ntiles;
+    const unsigned char *W = c.W;
+    const float *x = c.x;
+    int N = c.N, K = c.K, act = c.act;
+    const float *m = c.m, *r = c.r;
+    float *dst = c.dst;
+    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst};
+    return hipLaunchKernel(fn, dim3(grid), dim3(WAVES * kWave), args, lds, s);
+}
+
+template <int FMT> hipError_t launch_generic(const Call &c, hipStream_t s)
+{
+    const void *fn = reinterpret_cast<const void *>(&gemv_generic_kernel<FMT>);
+    int grid = (c.N + 3) / 4;
+    if (grid > 65536)
+        grid = 65536;
+    const unsigned char *W = c.W;
+    const float *x = c.x;
+    int N = c.N, K = c.K, act = c.act;
+    const float *m = c.m, *r = c.r;
+    float *dst = c.dst;
+    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst};
+    return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, s);
+}
+
+// The path depends only on (format, N, K, W alignment), never on the
+// epilogue, so a fused call and its unfused composition reduce identically.
+template <int FMT> hipError_t dispatch(const Call &c, hipStream_t s)
+{
+    const bool fast = (row_bytes<FMT>(c.K) % 16 == 0) && lds_bytes_fast<FMT>(c.K) <= kMaxLds;
+    if (!fast)
+        return launch_generic<FMT>(c, s);
+    if constexpr (FMT == GEMV_W_F32)
+        return launch_fast<FMT, 4, 1>(c, s);
+    else if constexpr (FMT == GEMV_W_F16 || FMT == GEMV_W_BF16)
+        return launch_fast<FMT, 4, 2>(c, s);
+    else if constexpr (FMT == GEMV_W_Q8B32)
+        return launch_fast<FMT, 4, 2>(c, s);
+    else
+        return launch_fast<FMT, 4, 4>(c, s);
+}
+
+int finish(hipError_t e)
+{
+    t_last_hip_error = (int)e;
+    return e == hipSuccess ? GEMV_OK : GEMV_E_HIP;
+}
+
+} // namespace
+} // namespace gemv
+
+extern "C" {
+
+int gemv_fused(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int act,
+               const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst, void *hip_stream)
+{
+    int st = gemv::validate(W, wfmt, N, K, x, act, mul_operand, add_operand, dst);
+    if (st != GEMV_OK)
+        return st;
+    gemv::Call c{static_cast<const unsigned char *>(W), x, (int)N, (int)K, act,
+                 mul_operand ? mul_operand->data : nullptr, add_operand ? add_operand->data : nullptr, dst->data};
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e;
+    switch (wfmt) {
+    case GEMV_W_F32:
+        e = gemv::dispatch<GEMV_W_F32>(c, s);
+        break;
+    case GEMV_W_F16:
+        e = gemv::dispatch<GEMV_W_F16>(c, s);
+        break;
+    case GEMV_W_BF16:
+        e = gemv::dispatch<GEMV_W_BF16>(c, s);
+        break;
+    case GEMV_W_Q8B32:
+        e = gemv::dispatch<GEMV_W_Q8B32>(c, s);
+        break;
+    default:
+        e = gemv::dispatch<GEMV_W_Q4B32>(c, s);
+        break;
+    }
+    return gemv::finish(e);
+}
+
+int gemv_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul_operand, const gemv_view *add_operand,
+                  const gemv_view *dst, void *hip_stream)
+{
+    int st = gemv::validate_epilogue(act, N, acc, mul_operand, add_operand, dst);
+    if (st != GEMV_OK)
+        return st;
+    int n = (int)N;
+    const float *m = mul_operand ? mul_operand->data : nullptr;
+    const float *r = add_operand ? add_operand->data : nullptr;
+    float *d = dst->data;
+    void *args[] = {&n, &acc, &act, &m, &r, &d};
+    int grid = (n + 255) / 256;
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemv::gemv_epilogue_kernel), dim3(grid), dim3(256),
+                                   args, 0, static_cast<hipStream_t>(hip_stream));
+    return gemv::finish(e);
+}
+
+int gemv_last_hip_error(void) { return gemv::t_last_hip_error; }
+
+} // extern "C"

@@ -1,0 +1,242 @@
+// Host-side argument checks for the fused decode GEMV: shapes, formats,
+// operand presence, contiguity, alignment and the overlap rule.  No HIP call
+// and no dereference of a device pointer, so it runs on a machine without a
+// GPU.  Stateless: nothing is remembered between calls (a guard that keeps
+// state across uses must be reset, as the closing comment of "vulkan: fuse
+// the sign multiply into the Hadamard FWHT" found; this one keeps none).
+//
+// The overlap rule follows "feat(cuda): fuse activations and residual add into
+// mmv f/q epilogues", "What changed", implementation notes: the destination
+// may alias the multiply/add operand element for element (an in-place op
+// reads and writes the same index) but must not alias the matmul inputs,
+// which are read across the whole reduction; operands must be contiguous and
+// of the same shape.  The operand guards of "ggml-cpu: fuse element-wise
+// epilogues (ADD, MUL, SILU) into ggml_compute_forward_mul_mat", "Guards",
+// add: f32, identically shaped (no broadcast), row-contiguous.
+#include "gemv_internal.h"
+
+#include <cstdint>
+
+namespace gemv {
+
+int64_t weight_bytes(int wfmt, int64_t N, int64_t K)
+{
+    if (wfmt < GEMV_W_F32 || wfmt > GEMV_W_Q4B32)
+        return GEMV_E_FMT;
+    if (N < 1 || K < 1 || N >= GEMV_MAX_DIM_EXTENT || K >= GEMV_MAX_DIM_EXTENT)
+        return GEMV_E_DIM;
+    switch (wfmt) {
+    case GEMV_W_F32:
+        return N * K * 4;
+    case GEMV_W_F16:
+    case GEMV_W_BF16:
+        return N * K * 2;
+    case GEMV_W_Q8B32:
+        if (K % 32)
+            return GEMV_E_DIM;
+        return align256(N * K) + N * (K / 32) * 2;
+    default: /* GEMV_W_Q4B32 */
+        if (K % 32)
+            return GEMV_E_DIM;
+        return align256(N * K / 2) + N * (K / 32) * 2;
+    }
+}
+
+namespace {
+
+struct Span {
+    uintptr_t lo, hi; // [lo, hi)
+};
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks one view: ndim, extents, C-contiguity (extent-1 strides ignored).
+// On success stores the element count.
+int check_view(const gemv_view *v, int64_t *numel)
+{
+    if (v->ndim < 1 || v->ndim > GEMV_MAX_DIMS)
+        return GEMV_E_LAYOUT;
+    int64_t n = 1;
+    for (int d = 0; d < v->ndim; ++d) {
+        if (v->shape[d] < 0)
+            return GEMV_E_LAYOUT;
+        if (v->shape[d] >= GEMV_MAX_DIM_EXTENT)
+            return GEMV_E_DIM;
+        n *= v->shape[d];
+        if (n >= GEMV_MAX_DIM_EXTENT)
+            return GEMV_E_DIM;
+    }
+    int64_t expect = 1;
+    for (int d = v->ndim - 1; d >= 0; --d) {
+        if (v->shape[d] != 1 && v->stride[d] != expect)
+            return GEMV_E_LAYOUT;
+        expect *= v->shape[d];
+    }
+    *numel = n;
+    return GEMV_OK;
+}
+
+bool same_shape(const gemv_view *a, const gemv_view *b)
+{
+    if (a->ndim != b->ndim)
+        return false;
+    for (int d = 0; d < a->ndim; ++d)
+        if (a->shape[d] != b->shape[d])
+            return false;
+    return true;
+}
+
+Span span_of(const void *p, int64_t bytes)
+{
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_act(int act) { return (act < GEMV_ACT_NONE || act > GEMV_ACT_ADD) ? GEMV_E_ACT : GEMV_OK; }
+
+bool uses_mul(int act) { return act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL; }
+bool uses_add(int act) { return act == GEMV_ACT_ADD; }
+
+// Operand presence, null data, layout of dst and the active operand, numel of
+// dst == N, 4-byte alignment.  Writes the active operand (or NULL).
+int check_epilogue_views(int act, int64_t N, const gemv_view *mul_operand, const gemv_view *add_operand,
+                         const gemv_view *dst, const gemv_view **operand)
+{
+    if (!dst || !dst->data)
+        return GEMV_E_NULL;
+    if ((mul_operand && !mul_operand->data) || (add_operand && !add_operand->data))
+        return GEMV_E_NULL;
+    if (uses_mul(act) != (mul_operand != nullptr) || uses_add(act) != (add_operand != nullptr))
+        return GEMV_E_OPERAND;
+    *operand = uses_mul(act) ? mul_operand : (uses_add(act) ? add_operand : nullptr);
+
+    int64_t nd = 0;
+    int st = check_view(dst, &nd);
+    if (st != GEMV_OK)
+        return st;
+    if (nd != N)
+        return GEMV_E_DIM;
+    if (*operand) {
+        int64_t no = 0;
+        st = check_view(*operand, &no);
+        if (st != GEMV_OK)
+            return st;
+        if (!same_shape(*operand, dst))
+            return GEMV_E_LAYOUT;
+    }
+    if (!aligned(dst->data, 4) || (*operand && !aligned((*operand)->data, 4)))
+        return GEMV_E_ALIGN;
+    return GEMV_OK;
+}
+
+} // namespace
+
+int validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int act,
+             const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst)
+{
+    if (!W || !x)
+        return GEMV_E_NULL;
+    if (wfmt < GEMV_W_F32 || wfmt > GEMV_W_Q4B32)
+        return GEMV_E_FMT;
+    int st = check_act(act);
+    if (st != GEMV_OK)
+        return st;
+    int64_t wbytes = weight_bytes(wfmt, N, K);
+    if (wbytes < 0)
+        return static_cast<int>(wbytes);
+
+    const gemv_view *operand = nullptr;
+    st = check_epilogue_views(act, N, mul_operand, add_operand, dst, &operand);
+    if (st != GEMV_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(x, 4))
+        return GEMV_E_ALIGN;
+
+    // dst never overlaps the matmul inputs; it overlaps the operand only as
+    // the identical view (same pointer; shapes are equal and both contiguous).
+    Span sd = span_of(dst->data, N * 4);
+    if (overlap(sd, span_of(W, wbytes)) || overlap(sd, span_of(x, K * 4)))
+        return GEMV_E_ALIAS;
+    if (operand && overlap(sd, span_of(operand->data, N * 4)) && operand->data != dst->data)
+        return GEMV_E_ALIAS;
+    return GEMV_OK;
+}
+
+int validate_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul_operand,
+                      const gemv_view *add_operand, const gemv_view *dst)
+{
+    if (!acc)
+        return GEMV_E_NULL;
+    int st = check_act(act);
+    if (st != GEMV_OK)
+        return st;
+    if (N < 1 || N >= GEMV_MAX_DIM_EXTENT)
+        return GEMV_E_DIM;
+    const gemv_view *operand = nullptr;
+    st = check_epilogue_views(act, N, mul_operand, add_operand, dst, &operand);
+    if (st != GEMV_OK)
+        return st;
+    if (!aligned(acc, 4))
+        return GEMV_E_ALIGN;
+    // Element-wise pass: dst may be the same memory as acc or the operand,
+    // never a shifted overlap of either.
+    Span sd = span_of(dst->data, N * 4);
+    if (overlap(sd, span_of(acc, N * 4)) && acc != dst->data)
+        return GEMV_E_ALIAS;
+    if (operand && overlap(sd, span_of(operand->data, N * 4)) && operand->data != dst->data)
+        return GEMV_E_ALIAS;
+    return GEMV_OK;
+}
+
+const char *strerror_of(int status)
+{
+    switch (status) {
+    case GEMV_OK:
+        return "ok";
+    case GEMV_E_NULL:
+        return "a required pointer is NULL";
+    case GEMV_E_DIM:
+        return "invalid dimensions (N, K < 1 or too large, K not a multiple of 32 for a block "
+               "format, or dst does not hold N elements)";
+    case GEMV_E_FMT:
+        return "unknown weight format";
+    case GEMV_E_ACT:
+        return "unknown epilogue";
+    case GEMV_E_OPERAND:
+        return "epilogue operand missing, or an unused operand was given";
+    case GEMV_E_LAYOUT:
+        return "view is not C-contiguous, has a bad rank or extent, or its shape differs from dst";
+    case GEMV_E_ALIAS:
+        return "dst overlaps W, x, or an operand other than as the identical view";
+    case GEMV_E_ALIGN:
+        return "misaligned pointer (W needs 16 bytes, f32 data 4 bytes)";
+    case GEMV_E_HIP:
+        return "HIP launch failed (see gemv_last_hip_error)";
+    default:
+        return "unknown status";
+    }
+}
+
+} // namespace gemv
+
+extern "C" {
+
+int gemv_validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int act,
+                  const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst)
+{
+    return gemv::validate(W, wfmt, N, K, x, act, mul_operand, add_operand, dst);
+}
+
+int gemv_epilogue_validate(int act, int64_t N, const float *acc, const gemv_view *mul_operand,
+                           const gemv_view *add_operand, const gemv_view *dst)
+{
+    return gemv::validate_epilogue(act, N, acc, mul_operand, add_operand, dst);
+}
+
+int64_t gemv_weight_bytes(int wfmt, int64_t N, int64_t K) { return gemv::weight_bytes(wfmt, N, K); }
+
+const char *gemv_strerror(int status) { return gemv::strerror_of(status); }
+
+} // extern "C"

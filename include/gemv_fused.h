@@ -1,0 +1,189 @@
+/*
+ * gemv_fused.h -- C ABI of the fused-epilogue decode GEMV for MI355X (gfx950).
+ *
+ * The library computes, for a weight matrix W of N rows by K columns and an
+ * f32 vector x of K values, the single-column product a_i = sum_j W_ij x_j
+ * (the decode case with one output column) and applies one element-wise
+ * epilogue to each a_i straight out of the accumulator, before the single
+ * store of the result.  One kernel launch per call; W is streamed once from
+ * HBM.
+ *
+ * Sources (web pages; the sections named are where each fact is stated):
+ *  - "feat(cuda): fuse activations and residual add into mmv f/q epilogues",
+ *    "Summary": the fusion applies to the matrix-vector kernels for float and
+ *    quantised weights on the decode path, one destination column.
+ *    "What changed": the tails sigmoid and silu, silu followed by a multiply
+ *    with a per-row operand, and a residual add that may reach the product
+ *    through a reshape; implementation notes: the activation is a run-time
+ *    switch (with a value meaning "none"), the result is written with the
+ *    matmul geometry into the final node's buffer, the destination may alias
+ *    the multiply/add operand element for element but never the matmul
+ *    inputs, and operands must be contiguous and of the same shape.
+ *    "Why": every folded tail saves a launch, and the residual add also saves
+ *    a write and a read of the output.
+ *  - "ggml-cpu: fuse element-wise epilogues (ADD, MUL, SILU) into
+ *    ggml_compute_forward_mul_mat", "What": the MUL_MAT + MUL pair (gate x up)
+ *    is the plain multiply tail.  "Guards": epilogue operands are f32,
+ *    identically shaped with no broadcast, row-contiguous and not transposed.
+ *    "Correctness": the fused result equals the unfused one (ADD and MUL bit
+ *    for bit).
+ *  - "vulkan: fuse the sign multiply into the Hadamard FWHT", closing comment:
+ *    an overlap guard must be reset between uses; here the checker keeps no
+ *    state at all between calls.
+ *
+ * Ownership and threading: the caller owns every buffer; all data pointers
+ * are device pointers (except where stated).  The library never allocates,
+ * frees, copies or synchronises, and keeps no pointer after a call returns.
+ * Calls are asynchronous on the given HIP stream (NULL = the null stream).
+ * The library is stateless apart from a thread-local last-HIP-error, so it may
+ * be called from several host threads.
+ */
+#ifndef GEMV_FUSED_H
+#define GEMV_FUSED_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats.  W is row-major: row n produces output n.
+ *  GEMV_W_F32   K f32 values per row (4 bytes each).
+ *  GEMV_W_F16   K IEEE binary16 values per row.
+ *  GEMV_W_BF16  K bfloat16 values per row.
+ *  GEMV_W_Q8B32 blocks of 32 int8 codes, one fp16 scale per block,
+ *               value = code * scale.  Byte image: the int8 code plane
+ *               [N][K] row-major, then at offset align256(N*K) the fp16 scale
+ *               plane [N][K/32] row-major.  K must be a multiple of 32.
+ *  GEMV_W_Q4B32 blocks of 32 unsigned 4-bit codes, one fp16 scale per block,
+ *               value = (code - 8) * scale.  Byte image: the nibble plane
+ *               [N][K/2] (byte k/2 of a row holds element k in its low nibble
+ *               when k is even, in its high nibble when k is odd), then at
+ *               offset align256(N*K/2) the fp16 scale plane [N][K/32].
+ *               K must be a multiple of 32.
+ * align256(v) rounds v up to a multiple of 256.  All multi-byte values are
+ * little-endian.  gemv_weight_bytes() gives the total byte count. */
+typedef enum {
+    GEMV_W_F32 = 0,
+    GEMV_W_F16 = 1,
+    GEMV_W_BF16 = 2,
+    GEMV_W_Q8B32 = 3,
+    GEMV_W_Q4B32 = 4
+} gemv_wfmt;
+
+/* Epilogues, applied to a = (W x)_i in f32:
+ *  NONE      y = a
+ *  SIGMOID   y = 1 / (1 + exp(-a))
+ *  SILU      y = a / (1 + exp(-a))
+ *  SILU_MUL  y = silu(a) * m_i      (needs mul_operand)
+ *  MUL       y = a * m_i            (needs mul_operand)
+ *  ADD       y = a + r_i            (needs add_operand)
+ * Exactly one epilogue per call. */
+typedef enum {
+    GEMV_ACT_NONE = 0,
+    GEMV_ACT_SIGMOID = 1,
+    GEMV_ACT_SILU = 2,
+    GEMV_ACT_SILU_MUL = 3,
+    GEMV_ACT_MUL = 4,
+    GEMV_ACT_ADD = 5
+} gemv_act;
+
+/* Status codes.  Every check runs before any launch; a rejected call
+ * launches nothing and writes nothing. */
+enum {
+    GEMV_OK = 0,
+    GEMV_E_NULL = -1,    /* a required pointer (W, x, acc, dst, a view's data) is NULL */
+    GEMV_E_DIM = -2,     /* N or K < 1 or too large, K % 32 != 0 for a block
+                            format, or the dst view does not hold N elements */
+    GEMV_E_FMT = -3,     /* unknown weight format */
+    GEMV_E_ACT = -4,     /* unknown epilogue */
+    GEMV_E_OPERAND = -5, /* the epilogue's operand is missing, or an operand it
+                            does not use is given */
+    GEMV_E_LAYOUT = -6,  /* ndim outside 1..4, a negative extent, a view that
+                            is not C-contiguous, or an operand whose shape
+                            differs from dst's */
+    GEMV_E_ALIAS = -7,   /* dst overlaps W, x or acc/operands other than by
+                            being the identical view */
+    GEMV_E_ALIGN = -8,   /* W not 16-byte aligned, or an f32 pointer not
+                            4-byte aligned */
+    GEMV_E_HIP = -9      /* the HIP launch failed; see gemv_last_hip_error() */
+};
+
+#define GEMV_MAX_DIMS 4
+#define GEMV_MAX_DIM_EXTENT (1LL << 31) /* N and K must be below this */
+
+/* A view of f32 device memory: element (i0, .., i_{ndim-1}) lives at
+ * data + sum_d i_d * stride[d] (strides in elements).  The library accepts
+ * only C-contiguous views (the stride of an extent-1 dimension is ignored),
+ * so element i of the flattened view, in C order, is data[i].  A reshape of
+ * the output (for example N = 4096 viewed as [32, 128]) is expressed by
+ * giving dst and the operand that shape; the kernel writes in matmul order,
+ * output row i to data[i]. */
+typedef struct {
+    float *data;
+    int32_t ndim;
+    int64_t shape[GEMV_MAX_DIMS];
+    int64_t stride[GEMV_MAX_DIMS];
+} gemv_view;
+
+/* dst = epilogue(W x), one launch on hip_stream.
+ *  W           device pointer to gemv_weight_bytes(wfmt, N, K) bytes in
+ *              format wfmt; 16-byte aligned.
+ *  N, K        rows (outputs) and columns (inputs) of W.
+ *  x           device pointer to K f32 values.
+ *  act         a gemv_act value.
+ *  mul_operand f32 view, same shape as dst; required by SILU_MUL and MUL,
+ *              must be NULL otherwise.
+ *  add_operand f32 view, same shape as dst; required by ADD, must be NULL
+ *              otherwise.
+ *  dst         f32 view holding N elements.  It may be the identical view of
+ *              the epilogue's operand (an in-place update: element i is read,
+ *              then written, by the same thread); it may not otherwise
+ *              overlap the operand, and it may never overlap W or x, which
+ *              every row reads across the whole reduction.
+ *  hip_stream  a hipStream_t, or NULL.
+ * Returns GEMV_OK or a negative status.  Asynchronous: returns after the
+ * launch is enqueued. */
+int gemv_fused(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int act,
+               const gemv_view *mul_operand, const gemv_view *add_operand,
+               const gemv_view *dst, void *hip_stream);
+
+/* The host-side checks of gemv_fused, with no HIP call and no dereference of
+ * any device pointer: returns the status gemv_fused would return before
+ * launching.  Safe on a machine with no GPU. */
+int gemv_validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int act,
+                  const gemv_view *mul_operand, const gemv_view *add_operand,
+                  const gemv_view *dst);
+
+/* The epilogue alone, as a separate element-wise pass (the unfused path):
+ * dst_i = epilogue(acc_i) for i < N, one launch on hip_stream.
+ *  acc         device pointer to N contiguous f32 values (a gemv_fused
+ *              result with act = NONE).
+ *  mul_operand, add_operand, dst: as for gemv_fused.  dst may be the same
+ *              memory as acc or as the operand (element for element); a
+ *              partial overlap is rejected.
+ * It uses the same device epilogue code as gemv_fused, so for the same a_i
+ * the fused and unfused results are identical. */
+int gemv_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul_operand,
+                  const gemv_view *add_operand, const gemv_view *dst, void *hip_stream);
+
+/* The host-side checks of gemv_epilogue; no HIP call. */
+int gemv_epilogue_validate(int act, int64_t N, const float *acc, const gemv_view *mul_operand,
+                           const gemv_view *add_operand, const gemv_view *dst);
+
+/* Size in bytes of an N x K weight matrix in format wfmt, or a negative
+ * status (GEMV_E_FMT, GEMV_E_DIM) when the arguments are invalid. */
+int64_t gemv_weight_bytes(int wfmt, int64_t N, int64_t K);
+
+/* A static, human-readable description of a status code. */
+const char *gemv_strerror(int status);
+
+/* The hipError_t of the last failed launch on the calling thread (0 if
+ * none); reset to 0 by every successful gemv_fused / gemv_epilogue call. */
+int gemv_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMV_FUSED_H */

@@ -1,0 +1,31 @@
+/*
+ * hbm_probe.h -- measurement helpers for the benchmark (not part of the GEMV
+ * library): a read-only HBM streaming probe, which sets the attainable read
+ * bandwidth beside the 8 TB/s specification, and a plain copy kernel of known
+ * size, whose FETCH_SIZE / WRITE_SIZE counter readings calibrate the
+ * counters' units.  Both launch one kernel on the given HIP stream and return
+ * 0, or a negative value on bad arguments, or the hipError_t of a failed
+ * launch (positive).  Device pointers; the caller owns all memory.
+ */
+#ifndef HBM_PROBE_H
+#define HBM_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads nbytes (a positive multiple of 16, buf 16-byte aligned) with 128-bit
+ * nontemporal loads; writes one f32 partial sum per workgroup to out[0..blocks). */
+int hbm_read_probe(const void *buf, int64_t nbytes, float *out, int blocks, void *hip_stream);
+
+/* dst[0..nbytes) = src[0..nbytes) with 128-bit loads and stores; nbytes a
+ * positive multiple of 16, both pointers 16-byte aligned, no overlap. */
+int hbm_copy(const void *src, void *dst, int64_t nbytes, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HBM_PROBE_H */

@@ -8,7 +8,7 @@ even an exact-order float32 sum fails it on random data.  The guarded metric
 divides instead by the larger of |y_i| and D_i, the first-order magnitude
 through which rounding in the dot product reaches the output:
 
-    err_i = |g_i - y_i| / max(|y_i|, D_i)
+    err_i = |g_i - y_i| / max(|y_i|, D_i, 2^-126)
 
 with a = acc_i, A = sum_j |w_ij x_j| (the oracle's absacc), s = sigmoid(a):
 
@@ -19,6 +19,9 @@ with a = acc_i, A = sum_j |w_ij x_j| (the oracle's absacc), s = sigmoid(a):
     mul       D = |m_i| A
     add       D = A + |r_i|
 
+The floor 2^-126 (the smallest normal float32) applies only to outputs in the
+subnormal range, where float32 carries absolute, not relative, precision.
+
 Any rounding of the float32 dot product obeys |acc_f32 - acc| <= c u A for a
 modest c, so a correct kernel gives err of order c * 2^-24 whatever the data;
 an indexing or layout mistake gives err of order 1.  The tolerances that gate
@@ -26,6 +29,8 @@ parity are per weight format: 1e-5 (f32), 2e-3 (f16, bf16) and 1e-4 (8-bit
 and 4-bit block formats, whose dequantised values are exact).
 """
 import numpy as np
+
+FLT32_MIN_NORMAL = 2.0 ** -126
 
 TOLERANCE = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "q8b32": 1e-4, "q4b32": 1e-4}
 
@@ -66,7 +71,7 @@ def compare(g, y, acc, absacc, act, m=None, r=None):
         return {"max_err": 0.0, "argmax": -1, "max_plain_rel": 0.0, "normwise": 0.0, "n": 0}
     D = error_scale(act, acc, absacc, m, r)
     diff = np.abs(g - y)
-    denom = np.maximum(np.abs(y), D)
+    denom = np.maximum(np.maximum(np.abs(y), D), FLT32_MIN_NORMAL)
     with np.errstate(divide="ignore", invalid="ignore"):
         err = np.where(diff == 0.0, 0.0, diff / denom)
         plain = np.where(diff == 0.0, 0.0, diff / np.abs(y))

@@ -1,0 +1,175 @@
+"""The C ABI on the host, with no GPU: the library loads, exports every
+function the header declares, and its checks return the documented status for
+every invalid-argument path.  Pointers here are plain integers; gemv_validate
+never dereferences them and makes no HIP call."""
+import os
+import re
+
+import pytest
+
+import oracle
+from decode_gemv_elementwise_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+S = b.STATUS_CODE
+
+W0 = 1 << 20            # fake device addresses, far apart
+X0 = 1 << 30
+D0 = 1 << 34
+M0 = 1 << 36
+R0 = 1 << 38
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gemv_fused.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = b.load()
+    names = declared_functions()
+    assert {"gemv_fused", "gemv_validate", "gemv_epilogue", "gemv_epilogue_validate", "gemv_weight_bytes",
+            "gemv_strerror", "gemv_last_hip_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in S.values():
+        assert b.gemv_strerror(code)
+    assert b.gemv_strerror(123) == "unknown status"
+    assert b.gemv_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "q8b32", "q4b32"])
+@pytest.mark.parametrize("N,K", [(1, 32), (4096, 4096), (14336, 4096), (4096, 14336), (3, 64), (32, 4096)])
+def test_weight_bytes_agrees_with_oracle(fmt, N, K):
+    assert b.gemv_weight_bytes(fmt, N, K) == oracle.weight_bytes(fmt, N, K)
+
+
+def test_weight_bytes_errors():
+    assert b.gemv_weight_bytes("q4b32", 4, 33) == S["GEMV_E_DIM"]
+    assert b.gemv_weight_bytes("f32", 0, 4) == S["GEMV_E_DIM"]
+    assert b.gemv_weight_bytes(7, 4, 4) == S["GEMV_E_FMT"]
+    assert b.gemv_weight_bytes("f32", 1 << 31, 4) == S["GEMV_E_DIM"]
+
+
+def v(addr, shape, stride=None):
+    return b.make_view(addr, shape, stride)
+
+
+def val(**kw):
+    args = dict(W=W0, wfmt="f32", N=64, K=64, x=X0, act="none", mul_operand=None, add_operand=None,
+                dst=v(D0, (64,)))
+    args.update(kw)
+    return b.gemv_validate(args["W"], args["wfmt"], args["N"], args["K"], args["x"], args["act"],
+                           args["mul_operand"], args["add_operand"], args["dst"])
+
+
+def test_valid_calls():
+    assert val() == S["GEMV_OK"]
+    for act in ("sigmoid", "silu"):
+        assert val(act=act) == S["GEMV_OK"]
+    assert val(act="silu_mul", mul_operand=v(M0, (64,))) == S["GEMV_OK"]
+    assert val(act="mul", mul_operand=v(M0, (64,))) == S["GEMV_OK"]
+    assert val(act="add", add_operand=v(R0, (64,))) == S["GEMV_OK"]
+    # the [32, 128] view of a 4096-row output, residual of the same shape
+    assert val(N=4096, K=6144, wfmt="q8b32", act="add", add_operand=v(R0, (32, 128)),
+               dst=v(D0, (32, 128))) == S["GEMV_OK"]
+    # in place: dst is the identical view of the operand
+    assert val(act="add", add_operand=v(R0, (64,)), dst=v(R0, (64,))) == S["GEMV_OK"]
+    assert val(act="mul", mul_operand=v(M0, (8, 8)), dst=v(M0, (8, 8))) == S["GEMV_OK"]
+    # extent-1 dimensions may carry any stride
+    assert val(dst=v(D0, (1, 64), (999, 1))) == S["GEMV_OK"]
+    # float formats accept any K
+    assert val(K=7) == S["GEMV_OK"]
+    assert val(wfmt="f16", K=1) == S["GEMV_OK"]
+    # read-only inputs may overlap each other (x inside W here)
+    assert val(x=W0 + 64) == S["GEMV_OK"]
+
+
+def test_null_pointers():
+    assert val(W=0) == S["GEMV_E_NULL"]
+    assert val(x=0) == S["GEMV_E_NULL"]
+    assert val(dst=None) == S["GEMV_E_NULL"]
+    assert val(dst=v(0, (64,))) == S["GEMV_E_NULL"]
+    assert val(act="add", add_operand=v(0, (64,))) == S["GEMV_E_NULL"]
+
+
+def test_format_and_act():
+    assert val(wfmt=5) == S["GEMV_E_FMT"]
+    assert val(wfmt=-1) == S["GEMV_E_FMT"]
+    assert val(act=6) == S["GEMV_E_ACT"]
+    assert val(act=-1) == S["GEMV_E_ACT"]
+
+
+def test_dimensions():
+    assert val(N=0, dst=v(D0, (0,))) == S["GEMV_E_DIM"]
+    assert val(K=0) == S["GEMV_E_DIM"]
+    assert val(K=-5) == S["GEMV_E_DIM"]
+    assert val(wfmt="q4b32", K=48) == S["GEMV_E_DIM"]
+    assert val(wfmt="q8b32", K=16) == S["GEMV_E_DIM"]
+    assert val(N=65, dst=v(D0, (64,))) == S["GEMV_E_DIM"]          # dst holds 64 != N
+    assert val(dst=v(D0, (8, 9))) == S["GEMV_E_DIM"]
+    assert val(K=1 << 31) == S["GEMV_E_DIM"]
+
+
+def test_operand_presence():
+    assert val(act="add") == S["GEMV_E_OPERAND"]
+    assert val(act="mul") == S["GEMV_E_OPERAND"]
+    assert val(act="silu_mul") == S["GEMV_E_OPERAND"]
+    assert val(act="none", add_operand=v(R0, (64,))) == S["GEMV_E_OPERAND"]
+    assert val(act="sigmoid", mul_operand=v(M0, (64,))) == S["GEMV_E_OPERAND"]
+    assert val(act="add", add_operand=v(R0, (64,)), mul_operand=v(M0, (64,))) == S["GEMV_E_OPERAND"]
+    assert val(act="mul", add_operand=v(R0, (64,))) == S["GEMV_E_OPERAND"]
+
+
+def test_layout():
+    assert val(dst=v(D0, (64,), (2,))) == S["GEMV_E_LAYOUT"]                      # strided
+    assert val(dst=v(D0, (8, 8), (1, 8))) == S["GEMV_E_LAYOUT"]                   # transposed
+    assert val(dst=v(D0, (1, 1, 1, 1, 64))) == S["GEMV_E_LAYOUT"]                 # rank 5
+    assert val(act="add", add_operand=v(R0, (8, 8)), dst=v(D0, (64,))) == S["GEMV_E_LAYOUT"]  # shape differs
+    assert val(act="add", add_operand=v(R0, (1, 64)), dst=v(D0, (64,))) == S["GEMV_E_LAYOUT"]  # no broadcast
+    assert val(act="add", add_operand=v(R0, (64,), (2,))) == S["GEMV_E_LAYOUT"]
+    assert val(dst=v(D0, (-64,))) == S["GEMV_E_LAYOUT"]
+
+
+def test_alignment():
+    assert val(W=W0 + 4) == S["GEMV_E_ALIGN"]
+    assert val(x=X0 + 2) == S["GEMV_E_ALIGN"]
+    assert val(dst=v(D0 + 1, (64,))) == S["GEMV_E_ALIGN"]
+    assert val(act="add", add_operand=v(R0 + 2, (64,))) == S["GEMV_E_ALIGN"]
+
+
+def test_alias_rules():
+    wbytes = 64 * 64 * 4
+    assert val(dst=v(W0, (64,))) == S["GEMV_E_ALIAS"]                       # dst on W
+    assert val(dst=v(W0 + wbytes - 4, (64,))) == S["GEMV_E_ALIAS"]          # last byte of W
+    assert val(dst=v(W0 + wbytes, (64,))) == S["GEMV_OK"]                   # just past W
+    assert val(dst=v(X0 - 252, (64,))) == S["GEMV_E_ALIAS"]                 # dst tail on x
+    assert val(dst=v(X0 - 256, (64,))) == S["GEMV_OK"]                      # touches, no overlap
+    assert val(dst=v(X0 + 64 * 4, (64,))) == S["GEMV_OK"]
+    # partial overlap with the operand is refused, identity is allowed
+    assert val(act="add", add_operand=v(R0, (64,)), dst=v(R0 + 4, (64,))) == S["GEMV_E_ALIAS"]
+    assert val(act="add", add_operand=v(R0 + 4, (64,)), dst=v(R0, (64,))) == S["GEMV_E_ALIAS"]
+    assert val(act="mul", mul_operand=v(M0, (64,)), dst=v(M0 + 252, (64,))) == S["GEMV_E_ALIAS"]
+    # the check is stateless: a refused call does not change the next verdict
+    assert val(act="add", add_operand=v(R0, (64,)), dst=v(R0, (64,))) == S["GEMV_OK"]
+
+
+def eval_(act="none", N=64, acc=X0, mul=None, add=None, dst=None):
+    return b.gemv_epilogue_validate(act, N, acc, mul, add, dst if dst is not None else v(D0, (N,)))
+
+
+def test_epilogue_validate():
+    assert eval_() == S["GEMV_OK"]
+    assert eval_(act="add", add=v(R0, (64,))) == S["GEMV_OK"]
+    assert eval_(act="add", add=v(R0, (64,)), dst=v(X0, (64,))) == S["GEMV_OK"]   # in place on acc
+    assert eval_(act="add", add=v(R0, (64,)), dst=v(R0, (64,))) == S["GEMV_OK"]   # in place on r
+    assert eval_(act="add", add=v(R0, (64,)), dst=v(X0 + 4, (64,))) == S["GEMV_E_ALIAS"]
+    assert eval_(act="add") == S["GEMV_E_OPERAND"]
+    assert eval_(acc=0) == S["GEMV_E_NULL"]
+    assert eval_(N=0, dst=v(D0, (0,))) == S["GEMV_E_DIM"]
+    assert eval_(act=17) == S["GEMV_E_ACT"]
+    assert eval_(acc=X0 + 1) == S["GEMV_E_ALIGN"]

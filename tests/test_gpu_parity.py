@@ -1,0 +1,320 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by
+element on the same seeded inputs, with the per-format tolerances of the
+guarded error metric (1e-5 f32, 2e-3 f16/bf16, 1e-4 block formats)."""
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from decode_gemv_elementwise_amd import binding, synth
+from gpu_util import check_parity, dev, host, log, run_fused
+
+pytestmark = pytest.mark.gpu
+
+ALL_ACTS = list(synth.ACTS)
+
+
+def _operands(rng, act, N):
+    m = synth.draw_vec(rng, N) if act in ("silu_mul", "mul") else None
+    r = synth.draw_vec(rng, N) if act == "add" else None
+    return m, r
+
+
+# ------------------------------------------------------------------ workloads at full size
+
+def _resolve(wl, name, outputs):
+    if name is None:
+        return None
+    if name.startswith("@"):
+        return outputs[name[1:]]
+    return wl.vectors[name]
+
+
+@pytest.mark.parametrize("wname", list(synth.WORKLOADS))
+def test_workload_calls_full_size(wname):
+    """Every call of every workload at its full size; all rows compared.  A
+    chained input (the multiplier of the up projection, the input of the down
+    projection) is the oracle's own f32-rounded output of the earlier call, fed
+    to both sides."""
+    wl = synth.WORKLOADS[wname](0)
+    outputs = {}
+    for c in wl.calls:
+        w = wl.weights[c.w]
+        x = _resolve(wl, c.x, outputs)
+        m = _resolve(wl, c.m, outputs)
+        r = _resolve(wl, c.r, outputs)
+        g, y, res = check_parity(w, x, c.act, m=m, r=r, out_shape=c.out_shape, inplace=c.inplace,
+                                 tag=f"{wname}/{c.name}")
+        log(f"  {c.name}: max_err={res['max_err']:.2e} plain_rel={res['max_plain_rel']:.2e}")
+        outputs[c.name] = y.astype(np.float32)
+
+
+# ------------------------------------------------------------------ every format x epilogue
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("act", ALL_ACTS)
+def test_format_epilogue_matrix(fmt, act):
+    rng = np.random.default_rng(zlib.crc32(f"{fmt}/{act}".encode()))
+    N, K = 300, 512
+    w = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    m, r = _operands(rng, act, N)
+    check_parity(w, x, act, m=m, r=r, tag=f"matrix {fmt}/{act}")
+
+
+# ------------------------------------------------------------------ odd, ragged and extreme shapes
+
+FLOAT_SHAPES = [(1, 1), (1, 7), (3, 64), (5, 4), (33, 257), (64, 1000), (17, 4097), (4097, 33),
+                (1000, 256), (1003, 4096), (2, 40960), (2, 40964), (65539, 8)]
+BLOCK_SHAPES = [(1, 32), (7, 64), (33, 96), (1000, 4096), (3, 32000), (2, 36384), (2, 36416), (1, 65536),
+                (4099, 32)]
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N,K", FLOAT_SHAPES)
+def test_float_shapes(fmt, N, K):
+    rng = np.random.default_rng(N * 7919 + K)
+    w = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    r = synth.draw_vec(rng, N)
+    check_parity(w, x, "add", r=r, tag=f"shape {fmt} {N}x{K}")
+
+
+@pytest.mark.parametrize("fmt", ["q8b32", "q4b32"])
+@pytest.mark.parametrize("N,K", BLOCK_SHAPES)
+def test_block_shapes(fmt, N, K):
+    rng = np.random.default_rng(N * 7919 + K + 1)
+    w = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    check_parity(w, x, "silu", tag=f"shape {fmt} {N}x{K}")
+
+
+# ------------------------------------------------------------------ exact cases
+
+def test_integer_exact_q8():
+    """Scale 1 and small integer x: every partial sum is an integer below 2^24,
+    so any summation order gives the same value: GPU == oracle bit for bit."""
+    log("integer exact q8")
+    rng = np.random.default_rng(3)
+    N, K = 1024, 6144
+    codes = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    w = synth.Weights("q8b32", N, K, synth.pack_q8b32(codes, np.ones((N, K // 32), np.float16)))
+    x = rng.integers(-3, 4, size=K).astype(np.float32)
+    g, _ = run_fused(w, x, "none")
+    acc, _ = oracle.gemv("q8b32", N, K, w.data, x)
+    assert np.array_equal(g.astype(np.float64), acc)
+
+
+def test_integer_exact_q4_and_f16():
+    log("integer exact q4 / f16")
+    rng = np.random.default_rng(4)
+    N, K = 512, 4096
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    w = synth.Weights("q4b32", N, K, synth.pack_q4b32(codes, np.ones((N, K // 32), np.float16)))
+    x = rng.integers(-4, 5, size=K).astype(np.float32)
+    g, _ = run_fused(w, x, "none")
+    acc, _ = oracle.gemv("q4b32", N, K, w.data, x)
+    assert np.array_equal(g.astype(np.float64), acc)
+    Wf = rng.integers(-8, 9, size=(N, K)).astype(np.float16)
+    wf = synth.Weights("f16", N, K, Wf.view(np.uint8).reshape(-1))
+    g, _ = run_fused(wf, x, "none")
+    acc, _ = oracle.gemv("f16", N, K, wf.data, x)
+    assert np.array_equal(g.astype(np.float64), acc)
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_zero_weights(fmt):
+    log(f"zero W {fmt}")
+    N, K = 130, 256
+    nb = synth.weight_nbytes(fmt, N, K)
+    data = np.zeros(nb, dtype=np.uint8)
+    if fmt == "q4b32":  # code 8 is value 0
+        data[: N * K // 2] = 0x88
+    w = synth.Weights(fmt, N, K, data)
+    rng = np.random.default_rng(1)
+    x = synth.draw_vec(rng, K)
+    m = synth.draw_vec(rng, N)
+    r = synth.draw_vec(rng, N)
+    want = {"none": 0.0, "sigmoid": 0.5, "silu": 0.0, "silu_mul": 0.0, "mul": 0.0}
+    for act, v in want.items():
+        g, _ = run_fused(w, x, act, m=m if act in ("silu_mul", "mul") else None)
+        assert np.all(g == v), (fmt, act)
+    g, _ = run_fused(w, x, "add", r=r)
+    assert np.array_equal(g, r)
+
+
+def test_identity_weights():
+    """4-bit identity (code 9 on the diagonal, 8 elsewhere, scale 1): the
+    accumulator is x exactly, so NONE returns x bit for bit."""
+    log("identity q4")
+    N = K = 4096
+    codes = np.full((N, K), 8, dtype=np.uint8)
+    np.fill_diagonal(codes, 9)
+    w = synth.Weights("q4b32", N, K, synth.pack_q4b32(codes, np.ones((N, K // 32), np.float16)))
+    x = synth.draw_vec(np.random.default_rng(2), K)
+    g, _ = run_fused(w, x, "none")
+    assert np.array_equal(g, x)
+    check_parity(w, x, "sigmoid", tag="identity sigmoid")
+
+
+# ------------------------------------------------------------------ fused == unfused, determinism
+
+def _fused_and_unfused(w, x, act, m, r):
+    Wd, xd = dev(w.data), dev(x)
+    md = dev(m) if m is not None else None
+    rd = dev(r) if r is not None else None
+    fused = torch.empty(w.N, dtype=torch.float32, device="cuda")
+    binding.gemv_fused(Wd, w.fmt, w.N, w.K, xd, act, mul_operand=md, add_operand=rd, dst=fused)
+    tmp = torch.empty(w.N, dtype=torch.float32, device="cuda")
+    unfused = torch.empty(w.N, dtype=torch.float32, device="cuda")
+    binding.gemv_fused(Wd, w.fmt, w.N, w.K, xd, "none", dst=tmp)
+    binding.gemv_epilogue(act, w.N, tmp, mul_operand=md, add_operand=rd, dst=unfused)
+    torch.cuda.synchronize()
+    return host(fused), host(unfused)
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_fused_equals_unfused_bitwise(fmt):
+    """The fused epilogue and the separate element-wise pass give identical
+    bits for every epilogue (ADD and MUL must; here SIGMOID/SILU/SILU_MUL do
+    too, since both paths run the same device function on the same value)."""
+    rng = np.random.default_rng(11)
+    N, K = 4099, 1024
+    w = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    for act in ALL_ACTS:
+        log(f"fused==unfused {fmt} {act}")
+        m, r = _operands(rng, act, N)
+        f, u = _fused_and_unfused(w, x, act, m, r)
+        assert np.array_equal(f.view(np.uint32), u.view(np.uint32)), (fmt, act)
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_deterministic(fmt):
+    log(f"determinism {fmt}")
+    rng = np.random.default_rng(12)
+    N, K = 2048, 4096
+    w = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    a, _ = run_fused(w, x, "silu")
+    b, _ = run_fused(w, x, "silu")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------------ aliasing and views
+
+def test_inplace_add_matches_out_of_place():
+    log("in-place add")
+    rng = np.random.default_rng(13)
+    w = synth.random_weights(rng, "f16", 4096, 4096)
+    x = synth.draw_vec(rng, 4096)
+    r = synth.draw_vec(rng, 4096)
+    g_in, _ = run_fused(w, x, "add", r=r, inplace=True)
+    g_out, _ = run_fused(w, x, "add", r=r)
+    assert np.array_equal(g_in, g_out)
+
+
+def test_inplace_mul_and_view_add():
+    log("in-place mul, [32,128] view add in place")
+    rng = np.random.default_rng(14)
+    w = synth.random_weights(rng, "q8b32", 4096, 6144)
+    x = synth.draw_vec(rng, 6144)
+    m = synth.draw_vec(rng, 4096)
+    check_parity(w, x, "mul", m=m, inplace=True, tag="q8 mul in place")
+    r = synth.draw_vec(rng, 4096).reshape(32, 128)
+    check_parity(w, x, "add", r=r, out_shape=(32, 128), inplace=True, tag="q8 view add in place")
+
+
+def test_rejected_call_writes_nothing():
+    log("rejected calls")
+    rng = np.random.default_rng(15)
+    w = synth.random_weights(rng, "f32", 64, 64)
+    Wd, xd = dev(w.data), dev(synth.draw_vec(rng, 64))
+    dst = torch.full((64,), 7.0, dtype=torch.float32, device="cuda")
+    r = torch.ones(64, dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.GemvError) as e:
+        binding.gemv_fused(Wd, "f32", 64, 64, xd, "add", dst=dst)  # missing residual
+    assert e.value.status == binding.STATUS_CODE["GEMV_E_OPERAND"]
+    with pytest.raises(binding.GemvError) as e:
+        binding.gemv_fused(Wd, "f32", 64, 64, xd, "add", add_operand=r[1:], dst=dst[:63])  # N mismatch
+    assert e.value.status == binding.STATUS_CODE["GEMV_E_DIM"]
+    with pytest.raises(binding.GemvError) as e:
+        binding.gemv_fused(Wd, "f32", 64, 64, xd, 9, dst=dst)
+    assert e.value.status == binding.STATUS_CODE["GEMV_E_ACT"]
+    alias = torch.zeros(80, dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.GemvError) as e:  # dst shifted by one element against the residual
+        binding.gemv_fused(Wd, "f32", 64, 64, xd, "add", add_operand=alias[:64], dst=alias[1:65])
+    assert e.value.status == binding.STATUS_CODE["GEMV_E_ALIAS"]
+    torch.cuda.synchronize()
+    assert torch.all(dst == 7.0)
+    assert torch.all(alias == 0.0)
+
+
+# ------------------------------------------------------------------ the 4-bit layer chain
+
+def test_layer_chain_fused_vs_unfused_and_gate_up_pairing():
+    """The six-GEMV 4-bit layer runs fused (6 launches) and unfused (6 GEMVs +
+    5 element-wise passes = 11 launches) with identical final bits; and
+    up * silu(gate) computed as MUL-after-SILU equals SILU_MUL-after-NONE."""
+    log("layer chain")
+    wl = synth.q4b32_decode_layer(0)
+    Wd = {k: dev(w.data) for k, w in wl.weights.items()}
+    V = {k: dev(v) for k, v in wl.vectors.items()}
+    ws = wl.weights
+
+    def f32(n):
+        return torch.empty(n, dtype=torch.float32, device="cuda")
+
+    def chain(fused: bool):
+        outs = {}
+        for c in wl.calls:
+            w = ws[c.w]
+            x = outs[c.x[1:]] if c.x.startswith("@") else V[c.x]
+            m = (outs[c.m[1:]] if c.m.startswith("@") else V[c.m]) if c.m else None
+            r = V[c.r] if c.r else None
+            out = f32(w.N)
+            if fused or c.act == "none":
+                binding.gemv_fused(Wd[c.w], "q4b32", w.N, w.K, x, c.act, mul_operand=m, add_operand=r, dst=out)
+            else:
+                tmp = f32(w.N)
+                binding.gemv_fused(Wd[c.w], "q4b32", w.N, w.K, x, "none", dst=tmp)
+                binding.gemv_epilogue(c.act, w.N, tmp, mul_operand=m, add_operand=r, dst=out)
+            outs[c.name] = out
+        torch.cuda.synchronize()
+        return {k: host(v) for k, v in outs.items()}
+
+    a, b = chain(True), chain(False)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+
+    # pairing: SILU on gate then MUL on up  ==  NONE on up then SILU_MUL on gate with m = up
+    g, u = ws["Wgate"], ws["Wup"]
+    up_raw = f32(u.N)
+    binding.gemv_fused(Wd["Wup"], "q4b32", u.N, u.K, V["x_ffn"], "none", dst=up_raw)
+    paired = f32(g.N)
+    binding.gemv_fused(Wd["Wgate"], "q4b32", g.N, g.K, V["x_ffn"], "silu_mul", mul_operand=up_raw, dst=paired)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(paired).view(np.uint32), a["q4_up_mul"].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt,lim", [("f32", 95.0), ("q4b32", 130.0)])
+def test_epilogue_extreme_accumulators(fmt, lim):
+    """Identity W makes the accumulator equal x exactly; x sweeps [-lim, lim],
+    through the range where e^-a overflows float32 (a < -88.7), so sigmoid and
+    silu must be evaluated without overflow."""
+    log(f"extreme accumulators {fmt} {lim}")
+    N = K = 512
+    x = np.linspace(-lim, lim, K).astype(np.float32)
+    x[:4] = [-88.8, -89.5, 88.8, 89.5]
+    if fmt == "f32":
+        w = synth.Weights("f32", N, K, np.eye(N, K, dtype=np.float32).view(np.uint8).reshape(-1))
+    else:
+        codes = np.full((N, K), 8, dtype=np.uint8)
+        np.fill_diagonal(codes, 9)
+        w = synth.Weights("q4b32", N, K, synth.pack_q4b32(codes, np.ones((N, K // 32), np.float16)))
+    m = synth.draw_vec(np.random.default_rng(5), N)
+    for act in ("sigmoid", "silu", "silu_mul"):
+        check_parity(w, x, act, m=m if act == "silu_mul" else None, tag=f"extreme {fmt} {act}")

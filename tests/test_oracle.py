@@ -350,3 +350,12 @@ def test_pins_catch_planted_mistakes(golden_dir):
     with pytest.raises(ValueError):
         oracle.gemv("f32", 12, 5, W.T.copy().view(np.uint8), x)
     assert acc.shape == (5,)
+
+
+def test_metric_subnormal_floor():
+    """Outputs below the smallest normal float32 are judged in absolute terms
+    against 2^-126 (float32 has only absolute precision there)."""
+    y = np.array([1e-45, -3e-40])
+    g = np.array([0.0, -2.9e-40])
+    res = compare(g, y, np.array([1e-45, -3e-40]), np.array([1e-50, 1e-50]), "none")
+    assert res["max_err"] == pytest.approx(1e-41 / 2.0 ** -126, rel=1e-9)
