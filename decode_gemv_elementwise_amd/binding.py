@@ -39,15 +39,17 @@ _I64 = ctypes.c_int64
 _VIEWP = ctypes.POINTER(GemvView)
 
 
-def load():
-    """Load libgemv_fused.so (build it with ``python -m decode_gemv_elementwise_amd.build``)."""
+def load(path=None):
+    """Load libgemv_fused.so (build it with ``python -m decode_gemv_elementwise_amd.build``).
+    ``path`` selects another build of the same library (the first load wins)."""
     global _LIB
     if _LIB is not None:
         return _LIB
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_gemv_elementwise_amd.build` "
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m decode_gemv_elementwise_amd.build` "
                           "(or __graft_entry__.build()) first")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     lib.gemv_fused.argtypes = [_VP, ctypes.c_int, _I64, _I64, _VP, ctypes.c_int, _VIEWP, _VIEWP, _VIEWP, _VP]
     lib.gemv_fused.restype = ctypes.c_int
     lib.gemv_validate.argtypes = [_VP, ctypes.c_int, _I64, _I64, _VP, ctypes.c_int, _VIEWP, _VIEWP, _VIEWP]

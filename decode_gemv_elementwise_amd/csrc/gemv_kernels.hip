@@ -67,7 +67,8 @@ __device__ __forceinline__ float silu_f(float a)
     return (a >= 0.0f ? a : a * t) / (1.0f + t);
 }
 
-__device__ __forceinline__ float apply_epilogue(int act, float a, const float *m, const float *r, int64_t i)
+// The epilogue of one output: v is m_i for SILU_MUL and MUL, r_i for ADD.
+__device__ __forceinline__ float apply_epilogue(int act, float a, float v)
 {
     switch (act) {
     case GEMV_ACT_SIGMOID:
@@ -76,15 +77,24 @@ __device__ __forceinline__ float apply_epilogue(int act, float a, const float *m
         return silu_f(a);
     case GEMV_ACT_SILU_MUL: {
         float s = silu_f(a);
-        return s * m[i];
+        return s * v;
     }
     case GEMV_ACT_MUL:
-        return a * m[i];
+        return a * v;
     case GEMV_ACT_ADD:
-        return a + r[i];
+        return a + v;
     default:
         return a;
     }
+}
+
+__device__ __forceinline__ float operand_of(int act, const float *m, const float *r, int64_t i)
+{
+    if (act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL)
+        return m[i];
+    if (act == GEMV_ACT_ADD)
+        return r[i];
+    return 0.0f;
 }
 
 // ------------------------------------------------------------------ wave reduce
@@ -191,6 +201,16 @@ template <> struct Fmt<GEMV_W_Q8B32> {
     }
 };
 
+// (d & mask) | bits in one VALU op.  The compiler emits an AND and an OR with
+// literal operands; v_and_or_b32 takes one constant from an SGPR and the other
+// from a VGPR (gfx9 VOP3 reads at most one scalar operand).
+__device__ __forceinline__ unsigned and_or(unsigned d, unsigned mask, unsigned bits)
+{
+    unsigned r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(d), "s"(mask), "v"(bits));
+    return r;
+}
+
 // 4-bit blocks: a chunk is one whole block of 32 codes.  A dword holds
 // elements 8i..8i+7, element k in bits 4k..4k+3.  OR-ing a nibble into the
 // mantissa of the f16 constant 1024 gives 1024 + c exactly (nibble at bit 0)
@@ -205,16 +225,17 @@ template <> struct Fmt<GEMV_W_Q4B32> {
     {
         const f16x2 off1 = {(_Float16)1032.0f, (_Float16)1032.0f};
         const f16x2 off16 = {(_Float16)1152.0f, (_Float16)1152.0f};
+        const unsigned magic = 0x64006400u;
         unsigned d[4] = {q.x, q.y, q.z, q.w};
         float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float *xi = xv + 8 * i;
-            unsigned e = d[i] >> 8;
-            f16x2 h0 = __builtin_bit_cast(f16x2, (d[i] & 0x000F000Fu) | 0x64006400u) - off1;  // c0-8, c4-8
-            f16x2 h1 = __builtin_bit_cast(f16x2, (d[i] & 0x00F000F0u) | 0x64006400u) - off16; // 16(c1-8), 16(c5-8)
-            f16x2 h2 = __builtin_bit_cast(f16x2, (e & 0x000F000Fu) | 0x64006400u) - off1;     // c2-8, c6-8
-            f16x2 h3 = __builtin_bit_cast(f16x2, (e & 0x00F000F0u) | 0x64006400u) - off16;    // 16(c3-8), 16(c7-8)
+            const unsigned e = d[i] >> 8;
+            f16x2 h0 = __builtin_bit_cast(f16x2, and_or(d[i], 0x000F000Fu, magic)) - off1;  // c0-8, c4-8
+            f16x2 h1 = __builtin_bit_cast(f16x2, and_or(d[i], 0x00F000F0u, magic)) - off16; // 16(c1-8), 16(c5-8)
+            f16x2 h2 = __builtin_bit_cast(f16x2, and_or(e, 0x000F000Fu, magic)) - off1;     // c2-8, c6-8
+            f16x2 h3 = __builtin_bit_cast(f16x2, and_or(e, 0x00F000F0u, magic)) - off16;    // 16(c3-8), 16(c7-8)
             a0 = fmaf((float)h0.x, xi[0], a0);
             a0 = fmaf((float)h0.y, xi[4], a0);
             a0 = fmaf((float)h2.x, xi[2], a0);
@@ -242,10 +263,127 @@ __device__ __forceinline__ float load_scale(const unsigned char *p)
 
 // ------------------------------------------------------------------ fast kernel
 // Requires: W 16-byte aligned, row_bytes(K) % 16 == 0, (K / E) * XS * 4 bytes
-// of LDS.  Grid: any number of workgroups; each takes tiles of WAVES * R rows
-// in a grid-stride loop.
+// of LDS.  One tile of WAVES * R rows per workgroup; wave w owns rows
+// tile*WAVES*R + w*R + [0, R).
+//
+// Lane l owns the 16-byte chunks l, l + 64, ... of each of its rows
+// (cpl = ceil(nchunks / 64) of them), fetched in batches of U chunks per row,
+// all loads of a batch issued before any is used; with more than one batch
+// the next is issued before the current one is consumed.
+//
+// No load sits behind a branch.  Chunks past the end of a row (a ragged last
+// batch) and rows past N are clamped to valid addresses and their
+// contributions discarded by a select; a branch around a load would make the
+// compiler wait for every outstanding load at the join.  Loads are issued in
+// the order they are needed (epilogue operand, x, then W), because the
+// hardware's load counter retires in order: waiting for x then does not wait
+// for W, and the barrier after staging waits only for LDS.
 
-template <int FMT, int WAVES, int R>
+template <int FMT, int R, int U> struct Batch {
+    u32x4 q[R][U];
+    float sc[R][U];
+};
+
+template <int FMT, int R, int U>
+__device__ __forceinline__ void issue_batch(Batch<FMT, R, U> &b, const unsigned char *const *wrow,
+                                            const unsigned char *const *srow, int lane, int jb, int nchunks)
+{
+    using F = Fmt<FMT>;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = min(lane + kWave * (jb + u), nchunks - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            b.q[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[r]) + c);
+            if constexpr (F::kBlock)
+                b.sc[r][u] = load_scale(srow[r] + 2 * (c / F::kChunksPerBlock));
+        }
+    }
+}
+
+template <int FMT, int R, int U>
+__device__ __forceinline__ void consume_batch(const Batch<FMT, R, U> &b, const float *xs, float *acc, int lane,
+                                              int jb, int nchunks)
+{
+    using F = Fmt<FMT>;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int craw = lane + kWave * (jb + u);
+        const bool valid = craw < nchunks;
+        const int c = min(craw, nchunks - 1);
+        float xv[F::E];
+        const f32x4 *xl = reinterpret_cast<const f32x4 *>(xs + c * F::XS);
+#pragma unroll
+        for (int i = 0; i < F::E / 4; ++i) {
+            f32x4 t = xl[i];
+            xv[4 * i] = t.x;
+            xv[4 * i + 1] = t.y;
+            xv[4 * i + 2] = t.z;
+            xv[4 * i + 3] = t.w;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float t;
+            if constexpr (F::kBlock)
+                t = F::dot(b.q[r][u], xv, b.sc[r][u], acc[r]);
+            else
+                t = F::dot(b.q[r][u], xv, acc[r]);
+            acc[r] = valid ? t : acc[r];
+        }
+    }
+}
+
+// x staging into LDS, in padded chunk order: a pass loads S float4 per thread
+// (indices clamped to the last float4; the duplicate writes that clamping
+// causes store the same value) and then writes them.  When a row is one batch
+// (U chunks per lane), K <= 64 * U * E, so S = ceil(E * U / (4 * WAVES)) loads
+// per thread cover x in one pass; longer rows take passes of 8.
+template <int FMT, int WAVES, int U, bool MULTI> constexpr int stage_loads()
+{
+    return MULTI ? 8 : (Fmt<FMT>::E * U + 4 * WAVES - 1) / (4 * WAVES);
+}
+
+template <int FMT, int kStage> struct XStage {
+    f32x4 v[kStage];
+    __device__ __forceinline__ void load(const float *x, int K, int base, bool aligned16)
+    {
+        const int nt = blockDim.x;
+        if (aligned16) {
+            const int n4 = K / 4;
+            const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+#pragma unroll
+            for (int j = 0; j < kStage; ++j)
+                v[j] = x4[min(base + j * nt + (int)threadIdx.x, n4 - 1)];
+        } else {
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int k = 4 * min(base + j * nt + (int)threadIdx.x, K / 4 - 1);
+                v[j] = f32x4{x[k], x[k + 1], x[k + 2], x[k + 3]};
+            }
+        }
+    }
+    __device__ __forceinline__ void store(float *xs, int K, int base) const
+    {
+        using F = Fmt<FMT>;
+        const int nt = blockDim.x;
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+            const int k = 4 * min(base + j * nt + (int)threadIdx.x, K / 4 - 1);
+            *reinterpret_cast<f32x4 *>(xs + (k / F::E) * F::XS + (k % F::E)) = v[j];
+        }
+    }
+};
+
+// Workgroup barrier for LDS only: waits for this wave's LDS writes, not for
+// its outstanding global loads.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int FMT, int WAVES, int R, int U, bool MULTI>
 __global__ __launch_bounds__(WAVES *kWave) void gemv_fast_kernel(const unsigned char *__restrict__ W,
                                                                  const float *__restrict__ x, int N, int K,
                                                                  int act, const float *mop, const float *rop,
@@ -255,77 +393,82 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_fast_kernel(const unsigned 
     extern __shared__ f32x4 lds4[];
     float *xs = reinterpret_cast<float *>(lds4);
 
-    const int nchunks = K / F::E;
-    // Stage x: 4 floats at a time (K % 4 == 0 here), into padded chunk order.
-    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
-        for (int k4 = threadIdx.x; k4 < K / 4; k4 += blockDim.x) {
-            int k = 4 * k4;
-            *reinterpret_cast<f32x4 *>(xs + (k / F::E) * F::XS + (k % F::E)) = x4[k4];
-        }
-    } else {
-        for (int k = threadIdx.x; k < K; k += blockDim.x)
-            xs[(k / F::E) * F::XS + (k % F::E)] = x[k];
-    }
-    __syncthreads();
-
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int rows_per_tile = WAVES * R;
-    const int ntiles = (N + rows_per_tile - 1) / rows_per_tile;
+    const int nchunks = K / F::E;
+    const int cpl = (nchunks + kWave - 1) / kWave;
+    const int nb = (cpl + U - 1) / U;
+    const int row0 = (blockIdx.x * WAVES + wave) * R;
     const int64_t rbytes = row_bytes<FMT>(K);
     const unsigned char *scales = F::kBlock ? W + align256_dev((int64_t)N * rbytes) : nullptr;
-    const int64_t scales_per_row = K / 32;
+    const int64_t sbytes = (int64_t)(K / 32) * 2;
 
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int row0 = tile * rows_per_tile + wave * R;
-        const unsigned char *wrow[R];
-        const unsigned char *srow[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            int row = min(row0 + r, N - 1);
-            wrow[r] = W + (int64_t)row * rbytes;
-            srow[r] = F::kBlock ? scales + (int64_t)row * scales_per_row * 2 : nullptr;
-        }
-        float acc[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            acc[r] = 0.0f;
+    // 1. epilogue operand of the row this lane stores (lane r stores row0 + r;
+    //    other lanes and rows past N read a clamped, valid element)
+    const bool has_op = act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL || act == GEMV_ACT_ADD;
+    const float *opp = act == GEMV_ACT_ADD ? rop : (has_op ? mop : x);
+    const int oplim = has_op ? N - 1 : K - 1;
+    const float opv = opp[min(row0 + min(lane, R - 1), oplim)];
 
-        for (int c = lane; c < nchunks; c += kWave) {
-            u32x4 q[R];
-            float sc[R];
+    // 2. x (first staging pass)
+    const bool x16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    constexpr int S = stage_loads<FMT, WAVES, U, MULTI>();
+    XStage<FMT, S> st;
+    st.load(x, K, 0, x16);
+
+    // 3. W, first batch
+    const unsigned char *wrow[R];
+    const unsigned char *srow[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[r]) + c);
-                if constexpr (F::kBlock)
-                    sc[r] = load_scale(srow[r] + 2 * (c / F::kChunksPerBlock));
-            }
-            float xv[F::E];
-            const f32x4 *xl = reinterpret_cast<const f32x4 *>(xs + c * F::XS);
+    for (int r = 0; r < R; ++r) {
+        const int row = min(row0 + r, N - 1);
+        wrow[r] = W + (int64_t)row * rbytes;
+        srow[r] = F::kBlock ? scales + (int64_t)row * sbytes : nullptr;
+    }
+    Batch<FMT, R, U> b0;
+    issue_batch<FMT, R, U>(b0, wrow, srow, lane, 0, nchunks);
+
+    // 4. finish staging
+    st.store(xs, K, 0);
+    for (int base = S * (int)blockDim.x; base < K / 4; base += S * (int)blockDim.x) {
+        st.load(x, K, base, x16);
+        st.store(xs, K, base);
+    }
+    lds_barrier();
+
+    // 5. stream the rows
+    float acc[R];
 #pragma unroll
-            for (int i = 0; i < F::E / 4; ++i) {
-                f32x4 t = xl[i];
-                xv[4 * i] = t.x;
-                xv[4 * i + 1] = t.y;
-                xv[4 * i + 2] = t.z;
-                xv[4 * i + 3] = t.w;
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if constexpr (F::kBlock)
-                    acc[r] = F::dot(q[r], xv, sc[r], acc[r]);
-                else
-                    acc[r] = F::dot(q[r], xv, acc[r]);
-            }
+    for (int r = 0; r < R; ++r)
+        acc[r] = 0.0f;
+    if constexpr (!MULTI) {
+        consume_batch<FMT, R, U>(b0, xs, acc, lane, 0, nchunks);
+    } else {
+        // several batches per row: double-buffered
+        Batch<FMT, R, U> b1;
+        int i = 0;
+        for (; i + 2 < nb; i += 2) {
+            issue_batch<FMT, R, U>(b1, wrow, srow, lane, (i + 1) * U, nchunks);
+            consume_batch<FMT, R, U>(b0, xs, acc, lane, i * U, nchunks);
+            issue_batch<FMT, R, U>(b0, wrow, srow, lane, (i + 2) * U, nchunks);
+            consume_batch<FMT, R, U>(b1, xs, acc, lane, (i + 1) * U, nchunks);
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float s = wave_sum(acc[r]);
-            int row = row0 + r;
-            if (lane == r && row < N)
-                dst[row] = apply_epilogue(act, s, mop, rop, row);
+        if (nb - i == 2) {
+            issue_batch<FMT, R, U>(b1, wrow, srow, lane, (i + 1) * U, nchunks);
+            consume_batch<FMT, R, U>(b0, xs, acc, lane, i * U, nchunks);
+            consume_batch<FMT, R, U>(b1, xs, acc, lane, (i + 1) * U, nchunks);
+        } else {
+            consume_batch<FMT, R, U>(b0, xs, acc, lane, i * U, nchunks);
         }
+    }
+
+    // 6. reduce, epilogue, store
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float s = wave_sum(acc[r]);
+        const int row = row0 + r;
+        if (lane == r && row < N)
+            dst[row] = apply_epilogue(act, s, opv);
     }
 }
 
@@ -369,7 +512,7 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(const unsigned char *
             acc = fmaf(weight_at<FMT>(W, N, K, row, k), x[k], acc);
         float s = wave_sum(acc);
         if (lane == 0)
-            dst[row] = apply_epilogue(act, s, mop, rop, row);
+            dst[row] = apply_epilogue(act, s, operand_of(act, mop, rop, row));
     }
 }
 
@@ -380,7 +523,7 @@ __global__ __launch_bounds__(256) void gemv_epilogue_kernel(int N, const float *
 {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < N)
-        dst[i] = apply_epilogue(act, acc[i], mop, rop, i);
+        dst[i] = apply_epilogue(act, acc[i], operand_of(act, mop, rop, i));
 }
 
 // ------------------------------------------------------------------ host dispatch
@@ -397,9 +540,9 @@ struct Call {
 
 template <int FMT> constexpr int lds_bytes_fast(int K) { return (K / Fmt<FMT>::E) * Fmt<FMT>::XS * 4; }
 
-template <int FMT, int WAVES, int R> hipError_t launch_fast(const Call &c, hipStream_t s)
+template <int FMT, int WAVES, int R, int U, bool MULTI> hipError_t launch_fast(const Call &c, hipStream_t s)
 {
-    const void *fn = reinterpret_cast<const void *>(&gemv_fast_kernel<FMT, WAVES, R>);
+    const void *fn = reinterpret_cast<const void *>(&gemv_fast_kernel<FMT, WAVES, R, U, MULTI>);
     size_t lds = (size_t)lds_bytes_fast<FMT>(c.K);
     if (lds > 64 * 1024) {
         static std::once_flag once;
@@ -409,8 +552,7 @@ template <int FMT, int WAVES, int R> hipError_t launch_fast(const Call &c, hipSt
             return attr_err;
     }
     const int rows_per_tile = WAVES * R;
-    int ntiles = (c.N + rows_per_tile - 1) / rows_per_tile;
-    int grid = ntiles;
+    const int grid = (c.N + rows_per_tile - 1) / rows_per_tile;
     const unsigned char *W = c.W;
     const float *x = c.x;
     int N = c.N, K = c.K, act = c.act;
@@ -435,21 +577,61 @@ template <int FMT> hipError_t launch_generic(const Call &c, hipStream_t s)
     return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, s);
 }
 
-// The path depends only on (format, N, K, W alignment), never on the
-// epilogue, so a fused call and its unfused composition reduce identically.
+#ifndef GEMV_WAVES
+#define GEMV_WAVES 8
+#endif
+#ifndef GEMV_LOADS_PER_LANE
+#define GEMV_LOADS_PER_LANE 8
+#endif
+constexpr int kWaves = GEMV_WAVES;            // waves per workgroup of the fast kernel
+constexpr int kLoadsPerLane = GEMV_LOADS_PER_LANE; // R * U target
+
+// Rows per wave for a batch of U chunk loads per row: about kLoadsPerLane
+// loads of 16 bytes per lane in flight.  A row longer than one batch (more
+// than 8 chunks per lane) is streamed one row per wave, double-buffered.
+template <int FMT, int U> hipError_t launch_u(const Call &c, hipStream_t s, bool multi)
+{
+    constexpr int R = U >= kLoadsPerLane ? 1 : (2 * U > kLoadsPerLane ? 1 : (4 * U > kLoadsPerLane ? 2 : (8 * U > kLoadsPerLane ? 4 : 8)));
+    if constexpr (U >= 5) {
+        if (multi)
+            return launch_fast<FMT, kWaves, 1, U, true>(c, s);
+    }
+    // Few rows: one row per wave so that more CUs take part.
+    const int64_t tiles = ((int64_t)c.N + kWaves * R - 1) / (kWaves * R);
+    if (R > 1 && tiles < 512)
+        return launch_fast<FMT, kWaves, 1, U, false>(c, s);
+    return launch_fast<FMT, kWaves, R, U, false>(c, s);
+}
+
+// The path depends only on (format, N, K), never on the epilogue, so a fused
+// call and its unfused composition reduce in the same order.
 template <int FMT> hipError_t dispatch(const Call &c, hipStream_t s)
 {
     const bool fast = (row_bytes<FMT>(c.K) % 16 == 0) && lds_bytes_fast<FMT>(c.K) <= kMaxLds;
     if (!fast)
         return launch_generic<FMT>(c, s);
-    if constexpr (FMT == GEMV_W_F32)
-        return launch_fast<FMT, 4, 1>(c, s);
-    else if constexpr (FMT == GEMV_W_F16 || FMT == GEMV_W_BF16)
-        return launch_fast<FMT, 4, 2>(c, s);
-    else if constexpr (FMT == GEMV_W_Q8B32)
-        return launch_fast<FMT, 4, 2>(c, s);
-    else
-        return launch_fast<FMT, 4, 4>(c, s);
+    const int nchunks = c.K / Fmt<FMT>::E;
+    const int cpl = (nchunks + kWave - 1) / kWave;
+    const int nbatch = (cpl + 7) / 8;
+    const int u = (cpl + nbatch - 1) / nbatch; // 1..8, batches of equal size
+    switch (u) {
+    case 1:
+        return launch_u<FMT, 1>(c, s, nbatch > 1);
+    case 2:
+        return launch_u<FMT, 2>(c, s, nbatch > 1);
+    case 3:
+        return launch_u<FMT, 3>(c, s, nbatch > 1);
+    case 4:
+        return launch_u<FMT, 4>(c, s, nbatch > 1);
+    case 5:
+        return launch_u<FMT, 5>(c, s, nbatch > 1);
+    case 6:
+        return launch_u<FMT, 6>(c, s, nbatch > 1);
+    case 7:
+        return launch_u<FMT, 7>(c, s, nbatch > 1);
+    default:
+        return launch_u<FMT, 8>(c, s, nbatch > 1);
+    }
 }
 
 int finish(hipError_t e)
