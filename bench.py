@@ -51,7 +51,28 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU-oracle sample length (0 disables the cpu_baseline leg)")
     p.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device copy of BYTES bytes, 5 times (calibrates the "
+                        "FETCH_SIZE / WRITE_SIZE counters against a known byte count), then exit")
     return p.parse_args()
+
+
+def copy_calibration(torch, nbytes):
+    import ctypes
+    from decode_gemv_elementwise_amd import build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    nbytes = (nbytes + 15) // 16 * 16
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.zeros_like(src)
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(5):
+        rc = lib.hbm_copy(src.data_ptr(), dst.data_ptr(), nbytes, s)
+        if rc != 0:
+            sys.exit(f"hbm_copy failed: {rc}")
+    torch.cuda.synchronize()
+    assert bool(torch.equal(src, dst))
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
 # ------------------------------------------------------------------ setup
@@ -351,6 +372,9 @@ def main():
     import torch
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
+    if args.copy_calibration > 0:
+        copy_calibration(torch, args.copy_calibration)
+        return
     from decode_gemv_elementwise_amd import binding, synth
     binding.load()  # fails loudly if the HIP library is not built
 

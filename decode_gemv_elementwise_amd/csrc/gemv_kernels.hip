@@ -99,9 +99,12 @@ __device__ __forceinline__ float operand_of(int act, const float *m, const float
 
 // ------------------------------------------------------------------ wave reduce
 
+// A DPP lane permutation of v.  Every pattern used below reads a valid lane,
+// so bound_ctrl is irrelevant to the result; setting it lets the compiler
+// fold the move into the consuming add (v_add_f32_dpp).
 template <int CTRL> __device__ __forceinline__ float dpp(float v)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float lane_read(float v, int l)
@@ -462,14 +465,16 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_fast_kernel(const unsigned 
         }
     }
 
-    // 6. reduce, epilogue, store
+    // 6. reduce each row; lane r takes row r's sum, one epilogue for all rows
+    float mine = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const float s = wave_sum(acc[r]);
-        const int row = row0 + r;
-        if (lane == r && row < N)
-            dst[row] = apply_epilogue(act, s, opv);
+        mine = lane == r ? s : mine;
     }
+    const float y = apply_epilogue(act, mine, opv);
+    if (lane < R && row0 + lane < N)
+        dst[row0 + lane] = y;
 }
 
 // ------------------------------------------------------------------ generic kernel
@@ -577,13 +582,18 @@ template <int FMT> hipError_t launch_generic(const Call &c, hipStream_t s)
     return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, s);
 }
 
-#ifndef GEMV_WAVES
-#define GEMV_WAVES 8
+// Waves per workgroup: float formats favour smaller workgroups (more of them
+// resident per CU), block formats larger ones (fewer copies of x staged).
+#ifndef GEMV_WAVES_FLOAT
+#define GEMV_WAVES_FLOAT 4
+#endif
+#ifndef GEMV_WAVES_BLOCK
+#define GEMV_WAVES_BLOCK 8
 #endif
 #ifndef GEMV_LOADS_PER_LANE
 #define GEMV_LOADS_PER_LANE 8
 #endif
-constexpr int kWaves = GEMV_WAVES;            // waves per workgroup of the fast kernel
+template <int FMT> constexpr int waves_of() { return Fmt<FMT>::kBlock ? GEMV_WAVES_BLOCK : GEMV_WAVES_FLOAT; }
 constexpr int kLoadsPerLane = GEMV_LOADS_PER_LANE; // R * U target
 
 // Rows per wave for a batch of U chunk loads per row: about kLoadsPerLane
@@ -591,6 +601,7 @@ constexpr int kLoadsPerLane = GEMV_LOADS_PER_LANE; // R * U target
 // than 8 chunks per lane) is streamed one row per wave, double-buffered.
 template <int FMT, int U> hipError_t launch_u(const Call &c, hipStream_t s, bool multi)
 {
+    constexpr int kWaves = waves_of<FMT>();
     constexpr int R = U >= kLoadsPerLane ? 1 : (2 * U > kLoadsPerLane ? 1 : (4 * U > kLoadsPerLane ? 2 : (8 * U > kLoadsPerLane ? 4 : 8)));
     if constexpr (U >= 5) {
         if (multi)
