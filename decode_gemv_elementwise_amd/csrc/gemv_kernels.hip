@@ -386,8 +386,17 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Optional occupancy floor (waves per SIMD) for the register allocator; 0 = none.
+#ifndef GEMV_MIN_WAVES_PER_SIMD
+#define GEMV_MIN_WAVES_PER_SIMD 0
+#endif
+template <int WAVES> constexpr int min_blocks_per_cu()
+{
+    return GEMV_MIN_WAVES_PER_SIMD > 0 ? (GEMV_MIN_WAVES_PER_SIMD * 4 + WAVES - 1) / WAVES : 1;
+}
+
 template <int FMT, int WAVES, int R, int U, bool MULTI>
-__global__ __launch_bounds__(WAVES *kWave) void gemv_fast_kernel(const unsigned char *__restrict__ W,
+__global__ __launch_bounds__(WAVES *kWave, min_blocks_per_cu<WAVES>()) void gemv_fast_kernel(const unsigned char *__restrict__ W,
                                                                  const float *__restrict__ x, int N, int K,
                                                                  int act, const float *mop, const float *rop,
                                                                  float *dst)
@@ -430,6 +439,9 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_fast_kernel(const unsigned 
     }
     Batch<FMT, R, U> b0;
     issue_batch<FMT, R, U>(b0, wrow, srow, lane, 0, nchunks);
+    // keep the W loads ahead of the staging stores (the scheduler may otherwise
+    // sink them below the wait for x, serialising the two round trips)
+    __builtin_amdgcn_sched_barrier(0);
 
     // 4. finish staging
     st.store(xs, K, 0);

@@ -68,7 +68,7 @@ def test_format_epilogue_matrix(fmt, act):
 # ------------------------------------------------------------------ odd, ragged and extreme shapes
 
 FLOAT_SHAPES = [(1, 1), (1, 7), (3, 64), (5, 4), (33, 257), (64, 1000), (17, 4097), (4097, 33),
-                (1000, 256), (1003, 4096), (2, 40960), (2, 40964), (65539, 8)]
+                (1000, 256), (1003, 4096), (300, 8192), (67, 14336), (2, 40960), (2, 40964), (65539, 8)]
 BLOCK_SHAPES = [(1, 32), (7, 64), (33, 96), (1000, 4096), (3, 32000), (2, 36384), (2, 36416), (1, 65536),
                 (4099, 32)]
 
