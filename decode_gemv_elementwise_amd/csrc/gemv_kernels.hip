@@ -406,7 +406,8 @@ __global__ __launch_bounds__(WAVES *kWave, min_blocks_per_cu<WAVES>()) void gemv
     float *xs = reinterpret_cast<float *>(lds4);
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    // uniform across the wave: row addresses are then computed on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nchunks = K / F::E;
     const int cpl = (nchunks + kWave - 1) / kWave;
     const int nb = (cpl + U - 1) / U;
@@ -605,6 +606,9 @@ template <int FMT> hipError_t launch_generic(const Call &c, hipStream_t s)
 #ifndef GEMV_LOADS_PER_LANE
 #define GEMV_LOADS_PER_LANE 8
 #endif
+#ifndef GEMV_MIN_TILES
+#define GEMV_MIN_TILES 512
+#endif
 template <int FMT> constexpr int waves_of() { return Fmt<FMT>::kBlock ? GEMV_WAVES_BLOCK : GEMV_WAVES_FLOAT; }
 constexpr int kLoadsPerLane = GEMV_LOADS_PER_LANE; // R * U target
 
@@ -619,9 +623,9 @@ template <int FMT, int U> hipError_t launch_u(const Call &c, hipStream_t s, bool
         if (multi)
             return launch_fast<FMT, kWaves, 1, U, true>(c, s);
     }
-    // Few rows: one row per wave so that more CUs take part.
+    // Fewer tiles than compute units: one row per wave so that more CUs take part.
     const int64_t tiles = ((int64_t)c.N + kWaves * R - 1) / (kWaves * R);
-    if (R > 1 && tiles < 512)
+    if (R > 1 && tiles < GEMV_MIN_TILES)
         return launch_fast<FMT, kWaves, 1, U, false>(c, s);
     return launch_fast<FMT, kWaves, R, U, false>(c, s);
 }

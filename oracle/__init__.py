@@ -57,6 +57,8 @@ def _lib():
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_epilogue.argtypes = [ctypes.c_int, ctypes.c_int64, _dp, _fp, _fp, _dp]
         lib.oracle_epilogue.restype = ctypes.c_int
+        lib.oracle_glu_epilogue.argtypes = [ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp]
+        lib.oracle_glu_epilogue.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -153,3 +155,23 @@ def reference(fmt, N, K, w, x, act, m=None, r=None, rows=None):
     ms = None if m is None else np.asarray(m, dtype=np.float32).reshape(-1)[b:e]
     rs = None if r is None else np.asarray(r, dtype=np.float32).reshape(-1)[b:e]
     return epilogue(act, acc, ms, rs), acc, absacc
+
+
+def glu_epilogue(act: str, g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """y = act(g) * u as its own pass (act: "silu" or "sigmoid"), in double."""
+    g = np.ascontiguousarray(g, dtype=np.float64).reshape(-1)
+    u = np.ascontiguousarray(u, dtype=np.float64).reshape(-1)
+    assert g.size == u.size
+    y = np.empty(g.size, dtype=np.float64)
+    rc = _lib().oracle_glu_epilogue(ACTS[act], g.size, _ptr(g, _dp), _ptr(u, _dp), _ptr(y, _dp))
+    if rc != 0:
+        raise ValueError(f"oracle_glu_epilogue failed for act={act}")
+    return y
+
+
+def glu_reference(fmt, N, K, w_gate, w_up, x, act="silu", rows=None):
+    """Gated pair: (y, g, absg, u, absu) over rows [begin, end), where g and u
+    are the gate and up row sums and y = act(g) * u."""
+    g, ag = gemv(fmt, N, K, w_gate, x, rows=rows)
+    u, au = gemv(fmt, N, K, w_up, x, rows=rows)
+    return glu_epilogue(act, g, u), g, ag, u, au

@@ -85,3 +85,32 @@ def compare(g, y, acc, absacc, act, m=None, r=None):
         "normwise": float(np.max(diff) / ymax) if ymax > 0 else float(np.max(diff)),
         "n": int(g.size),
     }
+
+
+def glu_error_scale(act, g, absg, u, absu):
+    """D for y = f(g) u: |f'(g) u| A_g + |f(g)| A_u (first-order propagation of
+    the two row sums' rounding), f = silu or sigmoid."""
+    g = np.asarray(g, dtype=np.float64).reshape(-1)
+    u = np.asarray(u, dtype=np.float64).reshape(-1)
+    s = _sigmoid(g)
+    if act == "silu":
+        f, df = g * s, s * (1.0 + g * (1.0 - s))
+    elif act == "sigmoid":
+        f, df = s, s * (1.0 - s)
+    else:
+        raise ValueError(act)
+    return np.abs(df * u) * np.asarray(absg, dtype=np.float64).reshape(-1) + np.abs(f) * np.asarray(absu, dtype=np.float64).reshape(-1)
+
+
+def compare_glu(gout, y, act, g, absg, u, absu):
+    """The guarded metric for the gated pair (same form as compare())."""
+    gout = np.asarray(gout, dtype=np.float64).reshape(-1)
+    y = np.asarray(y, dtype=np.float64).reshape(-1)
+    D = glu_error_scale(act, g, absg, u, absu)
+    diff = np.abs(gout - y)
+    denom = np.maximum(np.maximum(np.abs(y), D), FLT32_MIN_NORMAL)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(diff == 0.0, 0.0, diff / denom)
+    err = np.where(np.isnan(err), np.inf, err)
+    i = int(np.argmax(err)) if err.size else -1
+    return {"max_err": float(err[i]) if err.size else 0.0, "argmax": i, "n": int(gout.size)}

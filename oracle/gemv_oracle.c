@@ -227,3 +227,17 @@ int oracle_epilogue(int act, int64_t n, const double *acc, const float *m, const
     }
     return ORC_OK;
 }
+
+/* Gated pair of products over the same x (the gate/GLU fusion that the mmv
+ * kernels already had, per "feat(cuda): fuse activations and residual add
+ * into mmv f/q epilogues", Summary): y_i = act(g_i) * u_i, where g and u are
+ * the two row sums (each from oracle_gemv_rows, in double) and act is SILU
+ * or SIGMOID.  A separate pass, in double. */
+int oracle_glu_epilogue(int act, int64_t n, const double *g, const double *u, double *y)
+{
+    if (n < 0 || (act != ORC_SILU && act != ORC_SIGMOID))
+        return ORC_EBAD;
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = (act == ORC_SILU ? oracle_silu(g[i]) : oracle_sigmoid(g[i])) * u[i];
+    return ORC_OK;
+}

@@ -14,7 +14,7 @@ import scipy.special
 import torch
 
 import oracle
-from oracle.compare import TOLERANCE, compare, error_scale
+from oracle.compare import TOLERANCE, compare, error_scale, glu_error_scale
 from decode_gemv_elementwise_amd import synth
 
 U = 2.0 ** -53
@@ -359,3 +359,41 @@ def test_metric_subnormal_floor():
     g = np.array([0.0, -2.9e-40])
     res = compare(g, y, np.array([1e-45, -3e-40]), np.array([1e-50, 1e-50]), "none")
     assert res["max_err"] == pytest.approx(1e-41 / 2.0 ** -126, rel=1e-9)
+
+
+# ----------------------------------------------------------------- gated pair (GLU)
+
+def test_glu_closed_forms():
+    """Zero gate: silu(0) = 0 gives 0 and sigmoid(0) = 1/2 gives u/2; zero up
+    gives 0; identity gate with scipy's logistic."""
+    rng = np.random.default_rng(51)
+    N = K = 64
+    x = synth.draw_vec(rng, K)
+    wu = synth.random_weights(rng, "f16", N, K)
+    zero = np.zeros(N * K, dtype=np.float16).view(np.uint8)
+    u, _ = oracle.gemv("f16", N, K, wu.data, x)
+    y, *_ = oracle.glu_reference("f16", N, K, zero, wu.data, x, "silu")
+    assert np.all(y == 0.0)
+    y, *_ = oracle.glu_reference("f16", N, K, zero, wu.data, x, "sigmoid")
+    assert np.array_equal(y, 0.5 * u)
+    y, *_ = oracle.glu_reference("f16", N, K, wu.data, zero, x, "silu")
+    assert np.all(y == 0.0)
+    eye = np.eye(N, K, dtype=np.float16).view(np.uint8).reshape(-1)
+    y, *_ = oracle.glu_reference("f16", N, K, eye, wu.data, x, "silu")
+    xd = x.astype(np.float64)
+    assert np.allclose(y, xd * scipy.special.expit(xd) * u, rtol=1e-15, atol=0)
+    y, *_ = oracle.glu_reference("f16", N, K, eye, wu.data, x, "sigmoid")
+    assert np.allclose(y, scipy.special.expit(xd) * u, rtol=1e-15, atol=0)
+    with pytest.raises(ValueError):
+        oracle.glu_epilogue("add", u, u)
+
+
+def test_glu_metric_scale():
+    g = np.array([0.0, 1.5, -2.0])
+    u = np.array([2.0, -1.0, 0.5])
+    Ag = np.array([1.0, 2.0, 3.0])
+    Au = np.array([4.0, 5.0, 6.0])
+    s = scipy.special.expit(g)
+    d_silu = s * (1 + g * (1 - s))
+    assert np.allclose(glu_error_scale("silu", g, Ag, u, Au), np.abs(d_silu * u) * Ag + np.abs(g * s) * Au)
+    assert np.allclose(glu_error_scale("sigmoid", g, Ag, u, Au), np.abs(s * (1 - s) * u) * Ag + s * Au)
