@@ -113,6 +113,8 @@ class Step:
                         for c in self.calls}
         self.tmp_buf = {c.name: torch.zeros((R, wl.weights[c.w].N), dtype=torch.float32, device=dev)
                         for c in self.calls}
+        self.up_buf = {c.name: torch.zeros((R, wl.weights[c.w].N), dtype=torch.float32, device=dev)
+                       for c in self.calls if c.w2}
         self.prepared = []
         for i in range(R):
             self.prepared.append(self._prepare_set(binding, i, unfused))
@@ -140,7 +142,16 @@ class Step:
                 dst = r if c.act == "add" else m
             else:
                 dst = self.out_buf[c.name][i].view(shape)
-            if unfused and c.act != "none":
+            if c.w2:
+                W2 = self.w_buf[c.w2][i * self.w_slot[c.w2]:]
+                if unfused:  # up (none), gate (none), then silu(gate) * up
+                    up, tmp = self.up_buf[c.name][i], self.tmp_buf[c.name][i]
+                    fns.append(binding.PreparedCall(W2, w.fmt, w.N, w.K, x, "none", dst=up))
+                    fns.append(binding.PreparedCall(W, w.fmt, w.N, w.K, x, "none", dst=tmp))
+                    fns.append(_PreparedEpilogue(binding, "silu_mul", w.N, tmp, up, None, dst))
+                else:
+                    fns.append(binding.PreparedGlu(W, W2, w.fmt, w.N, w.K, x, c.act, dst=dst))
+            elif unfused and c.act != "none":
                 tmp = self.tmp_buf[c.name][i]
                 fns.append(binding.PreparedCall(W, w.fmt, w.N, w.K, x, "none", dst=tmp))
                 fns.append(_PreparedEpilogue(binding, c.act, w.N, tmp, m, r, dst))
@@ -152,7 +163,8 @@ class Step:
     def call_bytes(self, c):
         w = self.wl.weights[c.w]
         ops = (1 if c.m else 0) + (1 if c.r else 0)
-        return w.data.size + 4 * w.K + 4 * w.N * ops + 4 * w.N
+        w2 = self.wl.weights[c.w2].data.size if c.w2 else 0
+        return w.data.size + w2 + 4 * w.K + 4 * w.N * ops + 4 * w.N
 
     def launches_per_step(self):
         return len(self.prepared[0])
@@ -252,10 +264,14 @@ def cpu_baseline(wl, seconds):
             x = outputs[c.x[1:]] if c.x.startswith("@") else wl.vectors[c.x]
             m = (outputs[c.m[1:]] if c.m.startswith("@") else wl.vectors[c.m]) if c.m else None
             r = wl.vectors[c.r] if c.r else None
-            y, _, _ = oracle.reference(w.fmt, w.N, w.K, w.data, x, c.act, m=m, r=r)
+            if c.w2:
+                y = oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act)[0]
+            else:
+                y, _, _ = oracle.reference(w.fmt, w.N, w.K, w.data, x, c.act, m=m, r=r)
             outputs[c.name] = y.astype(np.float32)
             ops = (1 if c.m else 0) + (1 if c.r else 0)
-            nbytes += w.data.size + 4 * w.K + 4 * w.N * ops + 4 * w.N
+            w2 = wl.weights[c.w2].data.size if c.w2 else 0
+            nbytes += w.data.size + w2 + 4 * w.K + 4 * w.N * ops + 4 * w.N
             ncalls += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -313,8 +329,11 @@ def bench_workload(torch, binding, synth, name, args, probe):
             m = "_m_alone"
             vecs[m] = synth.draw_vec(np.random.default_rng(2), w.N)
         alone = synth.Call(dom.name, dom.w, x, dom.act, m=m, r=dom.r, out_shape=dom.out_shape,
-                           inplace=dom.inplace)
-        sub = synth.Workload(wl.name, {dom.w: w}, vecs, [alone])
+                           inplace=dom.inplace, w2=dom.w2)
+        ws = {dom.w: w}
+        if dom.w2:
+            ws[dom.w2] = wl.weights[dom.w2]
+        sub = synth.Workload(wl.name, ws, vecs, [alone])
         dstep = Step(torch, binding, sub, False)
         dom_sec = time_steps(torch, dstep, args.steps, args.warmup, args.launch) / args.steps
         del dstep
@@ -336,8 +355,8 @@ def bench_workload(torch, binding, synth, name, args, probe):
         "data": "synthetic",
         "config": {"workload": name, "calls": [
             {"name": c.name, "wfmt": wl.weights[c.w].fmt, "N": wl.weights[c.w].N, "K": wl.weights[c.w].K,
-             "epilogue": c.act + (" in place" if c.inplace else "") + (f" view {list(c.out_shape)}"
-                                                                      if c.out_shape else "")}
+             "epilogue": (f"{c.act}(gate) * up" if c.w2 else c.act) + (" in place" if c.inplace else "")
+             + (f" view {list(c.out_shape)}" if c.out_shape else "")}
             for c in wl.calls],
             "fused": not args.unfused, "launches_per_step": step.launches_per_step(),
             "launch": args.launch, "rotating_copies": step.copies,
@@ -347,7 +366,7 @@ def bench_workload(torch, binding, synth, name, args, probe):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": f"gemv_fast_kernel<{wl.weights[dom.w].fmt}> ({dom.name})",
+                     "kernel": f"gemv_fast_kernel<{wl.weights[dom.w].fmt}{', gated pair' if dom.w2 else ''}> ({dom.name})",
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "us_per_launch": round(dom_sec * 1e6, 3)},
     }

@@ -58,6 +58,10 @@ def load(path=None):
     lib.gemv_epilogue.restype = ctypes.c_int
     lib.gemv_epilogue_validate.argtypes = [ctypes.c_int, _I64, _VP, _VIEWP, _VIEWP, _VIEWP]
     lib.gemv_epilogue_validate.restype = ctypes.c_int
+    lib.gemv_glu.argtypes = [_VP, _VP, ctypes.c_int, _I64, _I64, _VP, ctypes.c_int, _VIEWP, _VP]
+    lib.gemv_glu.restype = ctypes.c_int
+    lib.gemv_glu_validate.argtypes = [_VP, _VP, ctypes.c_int, _I64, _I64, _VP, ctypes.c_int, _VIEWP]
+    lib.gemv_glu_validate.restype = ctypes.c_int
     lib.gemv_weight_bytes.argtypes = [ctypes.c_int, _I64, _I64]
     lib.gemv_weight_bytes.restype = _I64
     lib.gemv_strerror.argtypes = [ctypes.c_int]
@@ -175,6 +179,19 @@ def gemv_epilogue_validate(act, N, acc, mul_operand=None, add_operand=None, dst=
                                          _as_view(add_operand), _as_view(dst))
 
 
+def gemv_glu(W_gate, W_up, wfmt, N, K, x, act="silu", dst=None, stream=None):
+    """dst = act(W_gate x) * (W_up x) in one launch (act: "silu" or "sigmoid")."""
+    st = load().gemv_glu(_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, _addr(x), _act(act), _as_view(dst),
+                         _stream(stream))
+    if st != 0:
+        _raise(st)
+
+
+def gemv_glu_validate(W_gate, W_up, wfmt, N, K, x, act="silu", dst=None) -> int:
+    return load().gemv_glu_validate(_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, _addr(x), _act(act),
+                                    _as_view(dst))
+
+
 def gemv_weight_bytes(wfmt, N, K) -> int:
     return int(load().gemv_weight_bytes(_fmt(wfmt), N, K))
 
@@ -185,6 +202,21 @@ def gemv_strerror(status: int) -> str:
 
 def gemv_last_hip_error() -> int:
     return int(load().gemv_last_hip_error())
+
+
+class PreparedGlu:
+    """A gemv_glu call with its dst view marshalled once."""
+
+    def __init__(self, W_gate, W_up, wfmt, N, K, x, act="silu", dst=None):
+        self._lib = load()
+        self._view = dst if isinstance(dst, GemvView) else make_view(dst)
+        self._ptr = ctypes.pointer(self._view)
+        self._args = (_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, _addr(x), _act(act))
+
+    def __call__(self, stream=None):
+        st = self._lib.gemv_glu(*self._args, self._ptr, _stream(stream))
+        if st != 0:
+            _raise(st)
 
 
 class PreparedCall:

@@ -15,6 +15,8 @@ int validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int 
              const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst);
 int validate_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul_operand,
                       const gemv_view *add_operand, const gemv_view *dst);
+int validate_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,
+                 const gemv_view *dst);
 const char *strerror_of(int status);
 
 } // namespace gemv

@@ -395,12 +395,23 @@ template <int WAVES> constexpr int min_blocks_per_cu()
     return GEMV_MIN_WAVES_PER_SIMD > 0 ? (GEMV_MIN_WAVES_PER_SIMD * 4 + WAVES - 1) / WAVES : 1;
 }
 
-template <int FMT, int WAVES, int R, int U, bool MULTI>
+// The gated pair of products (GLU): W is the gate matrix and W2 the up matrix,
+// both streamed over the same staged x; the wave's batch holds R gate rows
+// followed by the same R up rows, and the epilogue is act(gate) * up.
+__device__ __forceinline__ float apply_glu(int act, float g, float u)
+{
+    const float a = act == GEMV_ACT_SIGMOID ? sigmoid_f(g) : silu_f(g);
+    return a * u;
+}
+
+template <int FMT, int WAVES, int R, int U, bool MULTI, bool GLU>
 __global__ __launch_bounds__(WAVES *kWave, min_blocks_per_cu<WAVES>()) void gemv_fast_kernel(const unsigned char *__restrict__ W,
+                                                                 const unsigned char *__restrict__ W2,
                                                                  const float *__restrict__ x, int N, int K,
                                                                  int act, const float *mop, const float *rop,
                                                                  float *dst)
 {
+    constexpr int RR = GLU ? 2 * R : R; // rows loaded per wave
     using F = Fmt<FMT>;
     extern __shared__ f32x4 lds4[];
     float *xs = reinterpret_cast<float *>(lds4);
@@ -414,6 +425,7 @@ __global__ __launch_bounds__(WAVES *kWave, min_blocks_per_cu<WAVES>()) void gemv
     const int row0 = (blockIdx.x * WAVES + wave) * R;
     const int64_t rbytes = row_bytes<FMT>(K);
     const unsigned char *scales = F::kBlock ? W + align256_dev((int64_t)N * rbytes) : nullptr;
+    const unsigned char *scales2 = (F::kBlock && GLU) ? W2 + align256_dev((int64_t)N * rbytes) : nullptr;
     const int64_t sbytes = (int64_t)(K / 32) * 2;
 
     // 1. epilogue operand of the row this lane stores (lane r stores row0 + r;
@@ -430,16 +442,20 @@ __global__ __launch_bounds__(WAVES *kWave, min_blocks_per_cu<WAVES>()) void gemv
     st.load(x, K, 0, x16);
 
     // 3. W, first batch
-    const unsigned char *wrow[R];
-    const unsigned char *srow[R];
+    const unsigned char *wrow[RR];
+    const unsigned char *srow[RR];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int row = min(row0 + r, N - 1);
         wrow[r] = W + (int64_t)row * rbytes;
         srow[r] = F::kBlock ? scales + (int64_t)row * sbytes : nullptr;
+        if constexpr (GLU) {
+            wrow[R + r] = W2 + (int64_t)row * rbytes;
+            srow[R + r] = F::kBlock ? scales2 + (int64_t)row * sbytes : nullptr;
+        }
     }
-    Batch<FMT, R, U> b0;
-    issue_batch<FMT, R, U>(b0, wrow, srow, lane, 0, nchunks);
+    Batch<FMT, RR, U> b0;
+    issue_batch<FMT, RR, U>(b0, wrow, srow, lane, 0, nchunks);
     // keep the W loads ahead of the staging stores (the scheduler may otherwise
     // sink them below the wait for x, serialising the two round trips)
     __builtin_amdgcn_sched_barrier(0);
@@ -453,39 +469,47 @@ __global__ __launch_bounds__(WAVES *kWave, min_blocks_per_cu<WAVES>()) void gemv
     lds_barrier();
 
     // 5. stream the rows
-    float acc[R];
+    float acc[RR];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RR; ++r)
         acc[r] = 0.0f;
     if constexpr (!MULTI) {
-        consume_batch<FMT, R, U>(b0, xs, acc, lane, 0, nchunks);
+        consume_batch<FMT, RR, U>(b0, xs, acc, lane, 0, nchunks);
     } else {
         // several batches per row: double-buffered
-        Batch<FMT, R, U> b1;
+        Batch<FMT, RR, U> b1;
         int i = 0;
         for (; i + 2 < nb; i += 2) {
-            issue_batch<FMT, R, U>(b1, wrow, srow, lane, (i + 1) * U, nchunks);
-            consume_batch<FMT, R, U>(b0, xs, acc, lane, i * U, nchunks);
-            issue_batch<FMT, R, U>(b0, wrow, srow, lane, (i + 2) * U, nchunks);
-            consume_batch<FMT, R, U>(b1, xs, acc, lane, (i + 1) * U, nchunks);
+            issue_batch<FMT, RR, U>(b1, wrow, srow, lane, (i + 1) * U, nchunks);
+            consume_batch<FMT, RR, U>(b0, xs, acc, lane, i * U, nchunks);
+            issue_batch<FMT, RR, U>(b0, wrow, srow, lane, (i + 2) * U, nchunks);
+            consume_batch<FMT, RR, U>(b1, xs, acc, lane, (i + 1) * U, nchunks);
         }
         if (nb - i == 2) {
-            issue_batch<FMT, R, U>(b1, wrow, srow, lane, (i + 1) * U, nchunks);
-            consume_batch<FMT, R, U>(b0, xs, acc, lane, i * U, nchunks);
-            consume_batch<FMT, R, U>(b1, xs, acc, lane, (i + 1) * U, nchunks);
+            issue_batch<FMT, RR, U>(b1, wrow, srow, lane, (i + 1) * U, nchunks);
+            consume_batch<FMT, RR, U>(b0, xs, acc, lane, i * U, nchunks);
+            consume_batch<FMT, RR, U>(b1, xs, acc, lane, (i + 1) * U, nchunks);
         } else {
-            consume_batch<FMT, R, U>(b0, xs, acc, lane, i * U, nchunks);
+            consume_batch<FMT, RR, U>(b0, xs, acc, lane, i * U, nchunks);
         }
     }
 
     // 6. reduce each row; lane r takes row r's sum, one epilogue for all rows
-    float mine = 0.0f;
+    float mine = 0.0f, mine2 = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const float s = wave_sum(acc[r]);
         mine = lane == r ? s : mine;
+        if constexpr (GLU) {
+            const float s2 = wave_sum(acc[R + r]);
+            mine2 = lane == r ? s2 : mine2;
+        }
     }
-    const float y = apply_epilogue(act, mine, opv);
+    float y;
+    if constexpr (GLU)
+        y = apply_glu(act, mine, mine2);
+    else
+        y = apply_epilogue(act, mine, opv);
     if (lane < R && row0 + lane < N)
         dst[row0 + lane] = y;
 }
@@ -517,20 +541,29 @@ template <int FMT> __device__ __forceinline__ float weight_at(const unsigned cha
     }
 }
 
-template <int FMT>
+template <int FMT, bool GLU>
 __global__ __launch_bounds__(256) void gemv_generic_kernel(const unsigned char *__restrict__ W,
+                                                           const unsigned char *__restrict__ W2,
                                                            const float *__restrict__ x, int N, int K, int act,
                                                            const float *mop, const float *rop, float *dst)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int nwaves = gridDim.x * (blockDim.x / kWave);
     for (int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; row < N; row += nwaves) {
-        float acc = 0.0f;
-        for (int k = lane; k < K; k += kWave)
+        float acc = 0.0f, acc2 = 0.0f;
+        for (int k = lane; k < K; k += kWave) {
             acc = fmaf(weight_at<FMT>(W, N, K, row, k), x[k], acc);
-        float s = wave_sum(acc);
+            if constexpr (GLU)
+                acc2 = fmaf(weight_at<FMT>(W2, N, K, row, k), x[k], acc2);
+        }
+        const float s = wave_sum(acc);
+        float y;
+        if constexpr (GLU)
+            y = apply_glu(act, s, wave_sum(acc2));
+        else
+            y = apply_epilogue(act, s, operand_of(act, mop, rop, row));
         if (lane == 0)
-            dst[row] = apply_epilogue(act, s, operand_of(act, mop, rop, row));
+            dst[row] = y;
     }
 }
 
@@ -550,6 +583,7 @@ thread_local int t_last_hip_error = 0;
 
 struct Call {
     const unsigned char *W;
+    const unsigned char *W2; // up matrix of a gated pair, else nullptr
     const float *x;
     int N, K, act;
     const float *m, *r;
@@ -558,9 +592,9 @@ struct Call {
 
 template <int FMT> constexpr int lds_bytes_fast(int K) { return (K / Fmt<FMT>::E) * Fmt<FMT>::XS * 4; }
 
-template <int FMT, int WAVES, int R, int U, bool MULTI> hipError_t launch_fast(const Call &c, hipStream_t s)
+template <int FMT, int WAVES, int R, int U, bool MULTI, bool GLU> hipError_t launch_fast(const Call &c, hipStream_t s)
 {
-    const void *fn = reinterpret_cast<const void *>(&gemv_fast_kernel<FMT, WAVES, R, U, MULTI>);
+    const void *fn = reinterpret_cast<const void *>(&gemv_fast_kernel<FMT, WAVES, R, U, MULTI, GLU>);
     size_t lds = (size_t)lds_bytes_fast<FMT>(c.K);
     if (lds > 64 * 1024) {
         static std::once_flag once;
@@ -571,27 +605,27 @@ template <int FMT, int WAVES, int R, int U, bool MULTI> hipError_t launch_fast(c
     }
     const int rows_per_tile = WAVES * R;
     const int grid = (c.N + rows_per_tile - 1) / rows_per_tile;
-    const unsigned char *W = c.W;
+    const unsigned char *W = c.W, *W2 = c.W2;
     const float *x = c.x;
     int N = c.N, K = c.K, act = c.act;
     const float *m = c.m, *r = c.r;
     float *dst = c.dst;
-    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst};
+    void *args[] = {&W, &W2, &x, &N, &K, &act, &m, &r, &dst};
     return hipLaunchKernel(fn, dim3(grid), dim3(WAVES * kWave), args, lds, s);
 }
 
-template <int FMT> hipError_t launch_generic(const Call &c, hipStream_t s)
+template <int FMT, bool GLU> hipError_t launch_generic(const Call &c, hipStream_t s)
 {
-    const void *fn = reinterpret_cast<const void *>(&gemv_generic_kernel<FMT>);
+    const void *fn = reinterpret_cast<const void *>(&gemv_generic_kernel<FMT, GLU>);
     int grid = (c.N + 3) / 4;
     if (grid > 65536)
         grid = 65536;
-    const unsigned char *W = c.W;
+    const unsigned char *W = c.W, *W2 = c.W2;
     const float *x = c.x;
     int N = c.N, K = c.K, act = c.act;
     const float *m = c.m, *r = c.r;
     float *dst = c.dst;
-    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst};
+    void *args[] = {&W, &W2, &x, &N, &K, &act, &m, &r, &dst};
     return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, s);
 }
 
@@ -615,49 +649,68 @@ constexpr int kLoadsPerLane = GEMV_LOADS_PER_LANE; // R * U target
 // Rows per wave for a batch of U chunk loads per row: about kLoadsPerLane
 // loads of 16 bytes per lane in flight.  A row longer than one batch (more
 // than 8 chunks per lane) is streamed one row per wave, double-buffered.
-template <int FMT, int U> hipError_t launch_u(const Call &c, hipStream_t s, bool multi)
+// A gated pair loads two rows (gate and up) per output row, so it takes half
+// as many output rows per wave.
+template <int FMT, int U, bool GLU> hipError_t launch_u(const Call &c, hipStream_t s, bool multi)
 {
     constexpr int kWaves = waves_of<FMT>();
-    constexpr int R = U >= kLoadsPerLane ? 1 : (2 * U > kLoadsPerLane ? 1 : (4 * U > kLoadsPerLane ? 2 : (8 * U > kLoadsPerLane ? 4 : 8)));
+    constexpr int R1 = U >= kLoadsPerLane ? 1 : (2 * U > kLoadsPerLane ? 1 : (4 * U > kLoadsPerLane ? 2 : (8 * U > kLoadsPerLane ? 4 : 8)));
+    constexpr int R = GLU ? (R1 > 1 ? R1 / 2 : 1) : R1;
     if constexpr (U >= 5) {
         if (multi)
-            return launch_fast<FMT, kWaves, 1, U, true>(c, s);
+            return launch_fast<FMT, kWaves, 1, U, true, GLU>(c, s);
     }
-    // Fewer tiles than compute units: one row per wave so that more CUs take part.
+    // Few tiles: one row per wave so that more CUs take part.
     const int64_t tiles = ((int64_t)c.N + kWaves * R - 1) / (kWaves * R);
     if (R > 1 && tiles < GEMV_MIN_TILES)
-        return launch_fast<FMT, kWaves, 1, U, false>(c, s);
-    return launch_fast<FMT, kWaves, R, U, false>(c, s);
+        return launch_fast<FMT, kWaves, 1, U, false, GLU>(c, s);
+    return launch_fast<FMT, kWaves, R, U, false, GLU>(c, s);
 }
 
 // The path depends only on (format, N, K), never on the epilogue, so a fused
 // call and its unfused composition reduce in the same order.
-template <int FMT> hipError_t dispatch(const Call &c, hipStream_t s)
+template <int FMT, bool GLU> hipError_t dispatch(const Call &c, hipStream_t s)
 {
     const bool fast = (row_bytes<FMT>(c.K) % 16 == 0) && lds_bytes_fast<FMT>(c.K) <= kMaxLds;
     if (!fast)
-        return launch_generic<FMT>(c, s);
+        return launch_generic<FMT, GLU>(c, s);
     const int nchunks = c.K / Fmt<FMT>::E;
     const int cpl = (nchunks + kWave - 1) / kWave;
     const int nbatch = (cpl + 7) / 8;
     const int u = (cpl + nbatch - 1) / nbatch; // 1..8, batches of equal size
     switch (u) {
     case 1:
-        return launch_u<FMT, 1>(c, s, nbatch > 1);
+        return launch_u<FMT, 1, GLU>(c, s, nbatch > 1);
     case 2:
-        return launch_u<FMT, 2>(c, s, nbatch > 1);
+        return launch_u<FMT, 2, GLU>(c, s, nbatch > 1);
     case 3:
-        return launch_u<FMT, 3>(c, s, nbatch > 1);
+        return launch_u<FMT, 3, GLU>(c, s, nbatch > 1);
     case 4:
-        return launch_u<FMT, 4>(c, s, nbatch > 1);
+        return launch_u<FMT, 4, GLU>(c, s, nbatch > 1);
     case 5:
-        return launch_u<FMT, 5>(c, s, nbatch > 1);
+        return launch_u<FMT, 5, GLU>(c, s, nbatch > 1);
     case 6:
-        return launch_u<FMT, 6>(c, s, nbatch > 1);
+        return launch_u<FMT, 6, GLU>(c, s, nbatch > 1);
     case 7:
-        return launch_u<FMT, 7>(c, s, nbatch > 1);
+        return launch_u<FMT, 7, GLU>(c, s, nbatch > 1);
     default:
-        return launch_u<FMT, 8>(c, s, nbatch > 1);
+        return launch_u<FMT, 8, GLU>(c, s, nbatch > 1);
+    }
+}
+
+template <bool GLU> hipError_t dispatch_any(int wfmt, const Call &c, hipStream_t s)
+{
+    switch (wfmt) {
+    case GEMV_W_F32:
+        return dispatch<GEMV_W_F32, GLU>(c, s);
+    case GEMV_W_F16:
+        return dispatch<GEMV_W_F16, GLU>(c, s);
+    case GEMV_W_BF16:
+        return dispatch<GEMV_W_BF16, GLU>(c, s);
+    case GEMV_W_Q8B32:
+        return dispatch<GEMV_W_Q8B32, GLU>(c, s);
+    default:
+        return dispatch<GEMV_W_Q4B32, GLU>(c, s);
     }
 }
 
@@ -678,28 +731,20 @@ int gemv_fused(const void *W, int wfmt, int64_t N, int64_t K, const float *x, in
     int st = gemv::validate(W, wfmt, N, K, x, act, mul_operand, add_operand, dst);
     if (st != GEMV_OK)
         return st;
-    gemv::Call c{static_cast<const unsigned char *>(W), x, (int)N, (int)K, act,
+    gemv::Call c{static_cast<const unsigned char *>(W), nullptr, x, (int)N, (int)K, act,
                  mul_operand ? mul_operand->data : nullptr, add_operand ? add_operand->data : nullptr, dst->data};
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    hipError_t e;
-    switch (wfmt) {
-    case GEMV_W_F32:
-        e = gemv::dispatch<GEMV_W_F32>(c, s);
-        break;
-    case GEMV_W_F16:
-        e = gemv::dispatch<GEMV_W_F16>(c, s);
-        break;
-    case GEMV_W_BF16:
-        e = gemv::dispatch<GEMV_W_BF16>(c, s);
-        break;
-    case GEMV_W_Q8B32:
-        e = gemv::dispatch<GEMV_W_Q8B32>(c, s);
-        break;
-    default:
-        e = gemv::dispatch<GEMV_W_Q4B32>(c, s);
-        break;
-    }
-    return gemv::finish(e);
+    return gemv::finish(gemv::dispatch_any<false>(wfmt, c, static_cast<hipStream_t>(hip_stream)));
+}
+
+int gemv_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,
+             const gemv_view *dst, void *hip_stream)
+{
+    int st = gemv::validate_glu(W_gate, W_up, wfmt, N, K, x, act, dst);
+    if (st != GEMV_OK)
+        return st;
+    gemv::Call c{static_cast<const unsigned char *>(W_gate), static_cast<const unsigned char *>(W_up), x, (int)N,
+                 (int)K, act, nullptr, nullptr, dst->data};
+    return gemv::finish(gemv::dispatch_any<true>(wfmt, c, static_cast<hipStream_t>(hip_stream)));
 }
 
 int gemv_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul_operand, const gemv_view *add_operand,

@@ -164,6 +164,32 @@ int validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int 
     return GEMV_OK;
 }
 
+// The gated pair: both matrices of one format and shape, the gate act SILU
+// or SIGMOID, dst (N f32, C-contiguous) overlapping neither matrix nor x.
+int validate_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,
+                 const gemv_view *dst)
+{
+    if (!W_gate || !W_up || !x)
+        return GEMV_E_NULL;
+    if (wfmt < GEMV_W_F32 || wfmt > GEMV_W_Q4B32)
+        return GEMV_E_FMT;
+    if (act != GEMV_ACT_SILU && act != GEMV_ACT_SIGMOID)
+        return GEMV_E_ACT;
+    int64_t wbytes = weight_bytes(wfmt, N, K);
+    if (wbytes < 0)
+        return static_cast<int>(wbytes);
+    const gemv_view *operand = nullptr;
+    int st = check_epilogue_views(GEMV_ACT_NONE, N, nullptr, nullptr, dst, &operand);
+    if (st != GEMV_OK)
+        return st;
+    if (!aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(x, 4))
+        return GEMV_E_ALIGN;
+    Span sd = span_of(dst->data, N * 4);
+    if (overlap(sd, span_of(W_gate, wbytes)) || overlap(sd, span_of(W_up, wbytes)) || overlap(sd, span_of(x, K * 4)))
+        return GEMV_E_ALIAS;
+    return GEMV_OK;
+}
+
 int validate_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul_operand,
                       const gemv_view *add_operand, const gemv_view *dst)
 {
@@ -233,6 +259,12 @@ int gemv_epilogue_validate(int act, int64_t N, const float *acc, const gemv_view
                            const gemv_view *add_operand, const gemv_view *dst)
 {
     return gemv::validate_epilogue(act, N, acc, mul_operand, add_operand, dst);
+}
+
+int gemv_glu_validate(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,
+                      const gemv_view *dst)
+{
+    return gemv::validate_glu(W_gate, W_up, wfmt, N, K, x, act, dst);
 }
 
 int64_t gemv_weight_bytes(int wfmt, int64_t N, int64_t K) { return gemv::weight_bytes(wfmt, N, K); }

@@ -20,6 +20,8 @@ Workloads (the decode shapes of a dense 4096-hidden / 14336-FFN layer):
   4096->6144 none, 4096->4096 +residual, 4096->14336 silu (gate),
   4096->14336 * gate output (up), 14336->4096 +residual (down, input = the up
   output), 4096->32 sigmoid.
+* ``q4b32_decode_layer_glu``: the same layer with gate and up as one gated
+  pair, silu(W_gate x) * (W_up x) (five calls).
 
 Draw order per workload, one ``numpy.random.default_rng(seed)`` each: weights
 (codes, then scales) in call order, then x, then m, then r.  Floats are drawn
@@ -147,6 +149,7 @@ class Call:
     r: Optional[str] = None
     out_shape: Optional[Tuple[int, ...]] = None  # view shape of dst (default [N])
     inplace: bool = False  # dst is the same memory as the add/mul operand
+    w2: Optional[str] = None  # up matrix of a gated pair: dst = act(w x) * (w2 x)
 
 
 @dataclass
@@ -217,12 +220,26 @@ def q4b32_decode_layer(seed: int = 0) -> Workload:
                     "six 4-bit block GEMVs of one decode layer, chained gate -> up -> down")
 
 
+def q4b32_decode_layer_glu(seed: int = 0) -> Workload:
+    """The same draws as q4b32_decode_layer, with the gate and up projections
+    issued as one gated pair (silu(W_gate x) * (W_up x)): five calls."""
+    wl = q4b32_decode_layer(seed)
+    calls = [Call("q4_qkv_none", "Wqkv", "x_qkv", "none"),
+             Call("q4_o_add", "Wo", "x_o", "add", r="r_o"),
+             Call("q4_gate_up_glu", "Wgate", "x_ffn", "silu", w2="Wup"),
+             Call("q4_down_add", "Wdown", "@q4_gate_up_glu", "add", r="r_down"),
+             Call("q4_gate_sigmoid_32", "Wg", "x_g", "sigmoid")]
+    return Workload("q4b32_decode_layer_glu", wl.weights, wl.vectors, calls,
+                    "the 4-bit decode layer with gate and up as one gated pair")
+
+
 WORKLOADS = {
     "f32_tiny_256": f32_tiny_256,
     "f16_outproj_residual_4096": f16_outproj_residual_4096,
     "bf16_swiglu_gate_14336x4096": bf16_swiglu_gate_14336x4096,
     "q8b32_view_residual_4096x6144": q8b32_view_residual_4096x6144,
     "q4b32_decode_layer": q4b32_decode_layer,
+    "q4b32_decode_layer_glu": q4b32_decode_layer_glu,
 }
 
 

@@ -148,6 +148,27 @@ int gemv_fused(const void *W, int wfmt, int64_t N, int64_t K, const float *x, in
                const gemv_view *mul_operand, const gemv_view *add_operand,
                const gemv_view *dst, void *hip_stream);
 
+/* The gated pair of products over one x (the gate fusion of the
+ * matrix-vector kernels that "feat(cuda): fuse activations and residual add
+ * into mmv f/q epilogues", Summary, leaves in place, and the gate x up product
+ * of "ggml-cpu: fuse element-wise epilogues (ADD, MUL, SILU) into
+ * ggml_compute_forward_mul_mat", What): one launch computes
+ *     dst_i = act((W_gate x)_i) * (W_up x)_i
+ * with act GEMV_ACT_SILU (SwiGLU) or GEMV_ACT_SIGMOID.  Both matrices have
+ * format wfmt and shape N x K (16-byte aligned; they may be the same memory);
+ * x is K f32 values; dst is an f32 view holding N elements that overlaps
+ * neither matrix nor x.  Each row sum is formed exactly as gemv_fused forms it,
+ * so the result equals gemv_fused(W_up, NONE) followed by
+ * gemv_fused(W_gate, SILU_MUL, m = that output) bit for bit.  Returns GEMV_OK
+ * or a negative status (GEMV_E_ACT for any other act); asynchronous on
+ * hip_stream; allocates nothing. */
+int gemv_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,
+             const gemv_view *dst, void *hip_stream);
+
+/* The host-side checks of gemv_glu; no HIP call. */
+int gemv_glu_validate(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x,
+                      int act, const gemv_view *dst);
+
 /* The host-side checks of gemv_fused, with no HIP call and no dereference of
  * any device pointer: returns the status gemv_fused would return before
  * launching.  Safe on a machine with no GPU. */

@@ -173,3 +173,33 @@ def test_epilogue_validate():
     assert eval_(N=0, dst=v(D0, (0,))) == S["GEMV_E_DIM"]
     assert eval_(act=17) == S["GEMV_E_ACT"]
     assert eval_(acc=X0 + 1) == S["GEMV_E_ALIGN"]
+
+
+U0 = 1 << 24  # a second fake weight matrix
+
+
+def gval(**kw):
+    args = dict(Wg=W0, Wu=U0, wfmt="f16", N=64, K=64, x=X0, act="silu", dst=v(D0, (64,)))
+    args.update(kw)
+    return b.gemv_glu_validate(args["Wg"], args["Wu"], args["wfmt"], args["N"], args["K"], args["x"], args["act"],
+                               args["dst"])
+
+
+def test_glu_validate():
+    assert gval() == S["GEMV_OK"]
+    assert gval(act="sigmoid") == S["GEMV_OK"]
+    assert gval(Wu=W0) == S["GEMV_OK"]                       # the same matrix twice is allowed
+    assert gval(dst=v(D0, (8, 8))) == S["GEMV_OK"]
+    for act in ("none", "silu_mul", "mul", "add", 9):
+        assert gval(act=act) == S["GEMV_E_ACT"]
+    assert gval(Wg=0) == S["GEMV_E_NULL"]
+    assert gval(Wu=0) == S["GEMV_E_NULL"]
+    assert gval(dst=None) == S["GEMV_E_NULL"]
+    assert gval(wfmt=5) == S["GEMV_E_FMT"]
+    assert gval(wfmt="q4b32", K=48) == S["GEMV_E_DIM"]
+    assert gval(N=65) == S["GEMV_E_DIM"]
+    assert gval(dst=v(D0, (64,), (2,))) == S["GEMV_E_LAYOUT"]
+    assert gval(Wu=U0 + 8) == S["GEMV_E_ALIGN"]
+    assert gval(dst=v(U0 + 64, (64,))) == S["GEMV_E_ALIAS"]   # dst on the up matrix
+    assert gval(dst=v(W0, (64,))) == S["GEMV_E_ALIAS"]        # dst on the gate matrix
+    assert gval(dst=v(X0, (64,))) == S["GEMV_E_ALIAS"]        # dst on x

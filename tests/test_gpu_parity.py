@@ -46,9 +46,13 @@ def test_workload_calls_full_size(wname):
         x = _resolve(wl, c.x, outputs)
         m = _resolve(wl, c.m, outputs)
         r = _resolve(wl, c.r, outputs)
-        g, y, res = check_parity(w, x, c.act, m=m, r=r, out_shape=c.out_shape, inplace=c.inplace,
-                                 tag=f"{wname}/{c.name}")
-        log(f"  {c.name}: max_err={res['max_err']:.2e} plain_rel={res['max_plain_rel']:.2e}")
+        if c.w2:
+            check_glu(w, wl.weights[c.w2], x, c.act, f"{wname}/{c.name}")
+            y = oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act)[0]
+        else:
+            g, y, res = check_parity(w, x, c.act, m=m, r=r, out_shape=c.out_shape, inplace=c.inplace,
+                                     tag=f"{wname}/{c.name}")
+            log(f"  {c.name}: max_err={res['max_err']:.2e} plain_rel={res['max_plain_rel']:.2e}")
         outputs[c.name] = y.astype(np.float32)
 
 
@@ -318,3 +322,84 @@ def test_epilogue_extreme_accumulators(fmt, lim):
     m = synth.draw_vec(np.random.default_rng(5), N)
     for act in ("sigmoid", "silu", "silu_mul"):
         check_parity(w, x, act, m=m if act == "silu_mul" else None, tag=f"extreme {fmt} {act}")
+
+
+# ------------------------------------------------------------------ gated pair (GLU)
+
+def _glu(wg, wu, x, act, out_shape=None):
+    Wg, Wu, xd = dev(wg.data), dev(wu.data), dev(x)
+    dst = torch.full(out_shape or (wg.N,), float("nan"), dtype=torch.float32, device="cuda")
+    binding.gemv_glu(Wg, Wu, wg.fmt, wg.N, wg.K, xd, act, dst=dst)
+    torch.cuda.synchronize()
+    return host(dst).reshape(-1)
+
+
+def check_glu(wg, wu, x, act, tag):
+    from oracle.compare import TOLERANCE, compare_glu
+    log(f"glu {tag} fmt={wg.fmt} N={wg.N} K={wg.K} act={act}")
+    g = _glu(wg, wu, x, act)
+    y, ga, gA, ua, uA = oracle.glu_reference(wg.fmt, wg.N, wg.K, wg.data, wu.data, x, act)
+    res = compare_glu(g, y, act, ga, gA, ua, uA)
+    assert np.all(np.isfinite(g)), tag
+    assert res["max_err"] <= TOLERANCE[wg.fmt], f"{tag}: {res}"
+    return g
+
+
+GLU_SHAPES = [(1, 32), (33, 96), (300, 512), (1003, 4096), (67, 14336), (17, 4128)]
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("N,K", GLU_SHAPES)
+def test_glu_parity(fmt, N, K):
+    rng = np.random.default_rng(zlib.crc32(f"glu/{fmt}/{N}/{K}".encode()))
+    wg = synth.random_weights(rng, fmt, N, K)
+    wu = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    for act in ("silu", "sigmoid"):
+        check_glu(wg, wu, x, act, f"{fmt} {N}x{K} {act}")
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16"])
+def test_glu_odd_k_generic_path(fmt):
+    rng = np.random.default_rng(61)
+    wg = synth.random_weights(rng, fmt, 40, 1001)
+    wu = synth.random_weights(rng, fmt, 40, 1001)
+    check_glu(wg, wu, synth.draw_vec(rng, 1001), "silu", f"{fmt} 40x1001")
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_glu_equals_composition_bitwise(fmt):
+    """gemv_glu(W_g, W_u) == gemv_fused(W_u, none) then gemv_fused(W_g, silu_mul, m = up), bit for bit."""
+    log(f"glu == composition {fmt}")
+    rng = np.random.default_rng(62)
+    N, K = 2050, 4096
+    wg = synth.random_weights(rng, fmt, N, K)
+    wu = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    Wg, Wu, xd = dev(wg.data), dev(wu.data), dev(x)
+    up = torch.empty(N, dtype=torch.float32, device="cuda")
+    comp = torch.empty(N, dtype=torch.float32, device="cuda")
+    binding.gemv_fused(Wu, fmt, N, K, xd, "none", dst=up)
+    binding.gemv_fused(Wg, fmt, N, K, xd, "silu_mul", mul_operand=up, dst=comp)
+    fused = torch.empty(N, dtype=torch.float32, device="cuda")
+    binding.gemv_glu(Wg, Wu, fmt, N, K, xd, "silu", dst=fused)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(fused).view(np.uint32), host(comp).view(np.uint32))
+
+
+def test_glu_full_size_layer_gate_up():
+    """The 4-bit layer's gate and up projections (14336 x 4096) as one gated pair."""
+    wl = synth.q4b32_decode_layer(0)
+    check_glu(wl.weights["Wgate"], wl.weights["Wup"], wl.vectors["x_ffn"], "silu", "q4 layer gate/up 14336x4096")
+
+
+def test_glu_rejected_writes_nothing():
+    rng = np.random.default_rng(63)
+    w = synth.random_weights(rng, "f16", 64, 64)
+    Wd, xd = dev(w.data), dev(synth.draw_vec(rng, 64))
+    dst = torch.full((64,), 3.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.GemvError) as e:
+        binding.gemv_glu(Wd, Wd, "f16", 64, 64, xd, "add", dst=dst)
+    assert e.value.status == binding.STATUS_CODE["GEMV_E_ACT"]
+    torch.cuda.synchronize()
+    assert torch.all(dst == 3.0)
