@@ -175,3 +175,29 @@ def glu_reference(fmt, N, K, w_gate, w_up, x, act="silu", rows=None):
     g, ag = gemv(fmt, N, K, w_gate, x, rows=rows)
     u, au = gemv(fmt, N, K, w_up, x, rows=rows)
     return glu_epilogue(act, g, u), g, ag, u, au
+
+
+def ncols_reference(fmt, N, K, w, X, act, M=None, R=None, rows=None):
+    """Several destination columns over one W: column b is the one-column
+    product of x_b = X[b] followed by the epilogue with the operand rows
+    M[b] / R[b].  The matrix-vector fusion of "feat(cuda): fuse activations
+    and residual add into mmv f/q epilogues" (Summary) is stated for one
+    destination column; this is its plain widening to ncols columns, each
+    column computed exactly as a separate one-column call.
+
+    X is float32 [ncols, K]; M and R are float32 [ncols, N] (or None).
+    Returns (Y, acc, absacc), each float64 [ncols, rows], row b of each being
+    destination column b (the b-major layout dst[b * N + i])."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim != 2 or X.shape[1] != K:
+        raise ValueError("X must be float32 [ncols, K]")
+    B = X.shape[0]
+    b0, e0 = (0, N) if rows is None else rows
+    Y = np.empty((B, e0 - b0))
+    acc = np.empty((B, e0 - b0))
+    absacc = np.empty((B, e0 - b0))
+    for b in range(B):
+        mb = None if M is None else np.asarray(M, dtype=np.float32).reshape(B, N)[b]
+        rb = None if R is None else np.asarray(R, dtype=np.float32).reshape(B, N)[b]
+        Y[b], acc[b], absacc[b] = reference(fmt, N, K, w, X[b], act, m=mb, r=rb, rows=(b0, e0))
+    return Y, acc, absacc

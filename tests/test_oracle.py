@@ -397,3 +397,79 @@ def test_glu_metric_scale():
     d_silu = s * (1 + g * (1 - s))
     assert np.allclose(glu_error_scale("silu", g, Ag, u, Au), np.abs(d_silu * u) * Ag + np.abs(g * s) * Au)
     assert np.allclose(glu_error_scale("sigmoid", g, Ag, u, Au), np.abs(s * (1 - s) * u) * Ag + s * Au)
+
+
+# ----------------------------------------------------------------- several columns (ncols)
+
+@pytest.mark.parametrize("fmt,N,K,B", [("f32", 3, 7, 3), ("f16", 4, 13, 2), ("q4b32", 3, 64, 4),
+                                       ("q8b32", 2, 32, 8)])
+def test_ncols_brute_force_exact(fmt, N, K, B):
+    """Each destination column against exact rational arithmetic over the
+    whole [ncols, K] input, and the residual add in the b-major layout."""
+    rng = np.random.default_rng(N * 100 + K + B)
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(B, K)).astype(np.float32)
+    Rr = rng.normal(size=(B, N)).astype(np.float32)
+    Y, acc, absacc = oracle.ncols_reference(fmt, N, K, w.data, X, "add", R=Rr)
+    assert Y.shape == acc.shape == absacc.shape == (B, N)
+    ex = _exact_values(w)
+    for b in range(B):
+        xf = [Fraction(float(v)) for v in X[b]]
+        for i in range(N):
+            exact = sum(ex[i][j] * xf[j] for j in range(K))
+            A = sum(abs(ex[i][j] * xf[j]) for j in range(K))
+            bound = gamma(max(K - 1, 0)) * float(A)
+            assert abs(float(Fraction(acc[b, i]) - exact)) <= bound * (1 + 1e-12) + 1e-300
+            assert abs(float(Fraction(absacc[b, i]) - A)) <= bound * (1 + 1e-12) + 1e-300
+            y_exact = exact + Fraction(float(Rr[b, i]))
+            assert abs(float(Fraction(Y[b, i]) - y_exact)) <= (bound + U * abs(float(y_exact))) * (1 + 1e-9) + 1e-300
+
+
+def _one_hot_columns(B, K, rng):
+    cols = rng.choice(K, size=B, replace=False)
+    X = np.zeros((B, K), dtype=np.float32)
+    X[np.arange(B), cols] = 1.0
+    return X, cols
+
+
+def test_ncols_one_hot_selects_weight_columns():
+    """x_b = e_{j_b}: column b of the output is column j_b of W exactly, and
+    the multiply tail takes its operand from row b of M (b-major)."""
+    rng = np.random.default_rng(61)
+    N, K, B = 40, 96, 5
+    w = synth.random_weights(rng, "q4b32", N, K)
+    X, cols = _one_hot_columns(B, K, rng)
+    M = rng.normal(size=(B, N)).astype(np.float32)
+    dense = (w.codes.astype(np.float64) - 8.0) * np.repeat(w.scales.astype(np.float64), 32, axis=1)
+    Y, acc, _ = oracle.ncols_reference("q4b32", N, K, w.data, X, "mul", M=M)
+    for b in range(B):
+        assert np.array_equal(acc[b], dense[:, cols[b]])
+        assert np.array_equal(Y[b], dense[:, cols[b]] * M[b].astype(np.float64))
+
+
+def test_ncols_single_column_rows_and_zero_x():
+    """One column reproduces the one-column result on any row slice; x = 0
+    gives epilogue(0) per column (ADD returns the residual row of its column)."""
+    rng = np.random.default_rng(62)
+    N, K, B = 33, 64, 3
+    w = synth.random_weights(rng, "bf16", N, K)
+    X = np.zeros((B, K), dtype=np.float32)
+    Rr = rng.normal(size=(B, N)).astype(np.float32)
+    Y, acc, _ = oracle.ncols_reference("bf16", N, K, w.data, X, "add", R=Rr)
+    assert np.all(acc == 0.0) and np.array_equal(Y, Rr.astype(np.float64))
+    Y, *_ = oracle.ncols_reference("bf16", N, K, w.data, X, "sigmoid", rows=(5, 20))
+    assert Y.shape == (B, 15) and np.all(Y == 0.5)
+
+
+def test_ncols_pins_catch_transposed_operand():
+    """A plausible layout mistake -- reading the [ncols, N] operand as
+    [N, ncols] -- fails the one-hot pin."""
+    rng = np.random.default_rng(63)
+    N, K, B = 24, 32, 3
+    w = synth.random_weights(rng, "f32", N, K)
+    X, cols = _one_hot_columns(B, K, rng)
+    M = rng.normal(size=(B, N)).astype(np.float32)
+    dense = w.data.view(np.float32).reshape(N, K).astype(np.float64)
+    wrong = M.reshape(N, B).T.copy()  # the mistaken reading
+    Y, *_ = oracle.ncols_reference("f32", N, K, w.data, X, "mul", M=wrong)
+    assert any(not np.array_equal(Y[b], dense[:, cols[b]] * M[b].astype(np.float64)) for b in range(B))
