@@ -28,9 +28,13 @@ import numpy as np  # noqa: E402
 
 METRIC = "fused GEMV achieved HBM GB/s (% of peak) and µs/call at decode shapes"
 PEAK_HBM_GBPS = 8000.0
+# f32 FMA throughput of the vector ALUs without packed FP32 (the kernels are
+# built with packed FP32 off): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
+PEAK_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 ROTATE_MIN_BYTES = 512 << 20
 DEFAULT_WORKLOAD = "f16_outproj_residual_4096"
-KERNEL_SOURCE = os.path.join(ROOT, "decode_gemv_elementwise_amd", "csrc", "gemv_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_gemv_elementwise_amd", "csrc", f)
+                  for f in ("gemv_device.h", "gemv_kernels.hip", "gemv_cols.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -78,7 +82,10 @@ def copy_calibration(torch, nbytes):
 # ------------------------------------------------------------------ setup
 
 def kernel_sha():
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def align(v, a=256):
@@ -109,9 +116,9 @@ class Step:
         for k, v in wl.vectors.items():
             t = torch.from_numpy(np.ascontiguousarray(v).reshape(-1)).to(dev)
             self.v_buf[k] = torch.stack([t.clone() for _ in range(R)])
-        self.out_buf = {c.name: torch.zeros((R, wl.weights[c.w].N), dtype=torch.float32, device=dev)
+        self.out_buf = {c.name: torch.zeros((R, c.ncols * wl.weights[c.w].N), dtype=torch.float32, device=dev)
                         for c in self.calls}
-        self.tmp_buf = {c.name: torch.zeros((R, wl.weights[c.w].N), dtype=torch.float32, device=dev)
+        self.tmp_buf = {c.name: torch.zeros((R, c.ncols * wl.weights[c.w].N), dtype=torch.float32, device=dev)
                         for c in self.calls}
         self.up_buf = {c.name: torch.zeros((R, wl.weights[c.w].N), dtype=torch.float32, device=dev)
                        for c in self.calls if c.w2}
@@ -135,7 +142,7 @@ class Step:
             w = self.wl.weights[c.w]
             W = self.w_buf[c.w][i * self.w_slot[c.w]:]
             x = self._vec(c.x, i)
-            shape = c.out_shape or (w.N,)
+            shape = c.out_shape or ((w.N,) if c.ncols == 1 else (c.ncols, w.N))
             m = self._vec(c.m, i, shape)
             r = self._vec(c.r, i, shape)
             if c.inplace:
@@ -151,6 +158,14 @@ class Step:
                     fns.append(_PreparedEpilogue(binding, "silu_mul", w.N, tmp, up, None, dst))
                 else:
                     fns.append(binding.PreparedGlu(W, W2, w.fmt, w.N, w.K, x, c.act, dst=dst))
+            elif c.ncols > 1:
+                if unfused and c.act != "none":
+                    tmp = self.tmp_buf[c.name][i].view(shape)
+                    fns.append(binding.PreparedNcols(W, w.fmt, w.N, w.K, c.ncols, x, "none", dst=tmp))
+                    fns.append(_PreparedEpilogue(binding, c.act, c.ncols * w.N, tmp, m, r, dst))
+                else:
+                    fns.append(binding.PreparedNcols(W, w.fmt, w.N, w.K, c.ncols, x, c.act, mul_operand=m,
+                                                     add_operand=r, dst=dst))
             elif unfused and c.act != "none":
                 tmp = self.tmp_buf[c.name][i]
                 fns.append(binding.PreparedCall(W, w.fmt, w.N, w.K, x, "none", dst=tmp))
@@ -164,7 +179,7 @@ class Step:
         w = self.wl.weights[c.w]
         ops = (1 if c.m else 0) + (1 if c.r else 0)
         w2 = self.wl.weights[c.w2].data.size if c.w2 else 0
-        return w.data.size + w2 + 4 * w.K + 4 * w.N * ops + 4 * w.N
+        return w.data.size + w2 + c.ncols * (4 * w.K + 4 * w.N * ops + 4 * w.N)
 
     def launches_per_step(self):
         return len(self.prepared[0])
@@ -266,12 +281,15 @@ def cpu_baseline(wl, seconds):
             r = wl.vectors[c.r] if c.r else None
             if c.w2:
                 y = oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act)[0]
+            elif c.ncols > 1:
+                y = oracle.ncols_reference(w.fmt, w.N, w.K, w.data, np.reshape(x, (c.ncols, w.K)), c.act,
+                                           M=m, R=r)[0].reshape(-1)
             else:
                 y, _, _ = oracle.reference(w.fmt, w.N, w.K, w.data, x, c.act, m=m, r=r)
             outputs[c.name] = y.astype(np.float32)
             ops = (1 if c.m else 0) + (1 if c.r else 0)
             w2 = wl.weights[c.w2].data.size if c.w2 else 0
-            nbytes += w.data.size + w2 + 4 * w.K + 4 * w.N * ops + 4 * w.N
+            nbytes += w.data.size + w2 + c.ncols * (4 * w.K + 4 * w.N * ops + 4 * w.N)
             ncalls += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -324,12 +342,12 @@ def bench_workload(torch, binding, synth, name, args, probe):
         x, m = dom.x, dom.m
         if x.startswith("@"):
             x = "_x_alone"
-            vecs[x] = synth.draw_vec(np.random.default_rng(1), w.K)
+            vecs[x] = synth.draw_vec(np.random.default_rng(1), dom.ncols * w.K)
         if m and m.startswith("@"):
             m = "_m_alone"
-            vecs[m] = synth.draw_vec(np.random.default_rng(2), w.N)
+            vecs[m] = synth.draw_vec(np.random.default_rng(2), dom.ncols * w.N)
         alone = synth.Call(dom.name, dom.w, x, dom.act, m=m, r=dom.r, out_shape=dom.out_shape,
-                           inplace=dom.inplace, w2=dom.w2)
+                           inplace=dom.inplace, w2=dom.w2, ncols=dom.ncols)
         ws = {dom.w: w}
         if dom.w2:
             ws[dom.w2] = wl.weights[dom.w2]
@@ -338,7 +356,13 @@ def bench_workload(torch, binding, synth, name, args, probe):
         dom_sec = time_steps(torch, dstep, args.steps, args.warmup, args.launch) / args.steps
         del dstep
     dom_bytes = step.call_bytes(dom)
+    dom_w = wl.weights[dom.w]
+    dom_flops = 2 * dom_w.N * dom_w.K * dom.ncols * (2 if dom.w2 else 1)
     achieved = dom_bytes / dom_sec / 1e9
+    if dom.ncols > 1:
+        kernel_name = f"gemv_cols_kernel<{dom_w.fmt}, ncols={dom.ncols}> ({dom.name})"
+    else:
+        kernel_name = f"gemv_fast_kernel<{dom_w.fmt}{', gated pair' if dom.w2 else ''}> ({dom.name})"
     traffic = read_counters(name)
     res = {
         "metric": METRIC,
@@ -356,7 +380,7 @@ def bench_workload(torch, binding, synth, name, args, probe):
         "config": {"workload": name, "calls": [
             {"name": c.name, "wfmt": wl.weights[c.w].fmt, "N": wl.weights[c.w].N, "K": wl.weights[c.w].K,
              "epilogue": (f"{c.act}(gate) * up" if c.w2 else c.act) + (" in place" if c.inplace else "")
-             + (f" view {list(c.out_shape)}" if c.out_shape else "")}
+             + (f" view {list(c.out_shape)}" if c.out_shape else ""), **({"ncols": c.ncols} if c.ncols > 1 else {})}
             for c in wl.calls],
             "fused": not args.unfused, "launches_per_step": step.launches_per_step(),
             "launch": args.launch, "rotating_copies": step.copies,
@@ -366,10 +390,18 @@ def bench_workload(torch, binding, synth, name, args, probe):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": f"gemv_fast_kernel<{wl.weights[dom.w].fmt}{', gated pair' if dom.w2 else ''}> ({dom.name})",
+                     "kernel": kernel_name,
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "us_per_launch": round(dom_sec * 1e6, 3)},
     }
+    # one FMA per weight and destination column: where that work at the VALU
+    # peak takes longer than the bytes at the HBM peak, the ALU is the roof
+    if dom_flops / (PEAK_VALU_TFLOPS * 1e12) > dom_bytes / (PEAK_HBM_GBPS * 1e9):
+        tflops = dom_flops / dom_sec / 1e12
+        res["roofline"].update({"bound": "alu", "achieved": round(tflops, 3), "peak": round(PEAK_VALU_TFLOPS, 1),
+                                "unit": "TFLOP/s", "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
+                                "algorithmic_flops_per_launch": dom_flops,
+                                "hbm_gbps": round(achieved, 2)})
     if probe is not None:
         res["probe_read_gbps"] = round(probe, 1)
         res["roofline"]["frac_of_probe"] = round(achieved / probe, 4)

@@ -62,6 +62,12 @@ def load(path=None):
     lib.gemv_glu.restype = ctypes.c_int
     lib.gemv_glu_validate.argtypes = [_VP, _VP, ctypes.c_int, _I64, _I64, _VP, ctypes.c_int, _VIEWP]
     lib.gemv_glu_validate.restype = ctypes.c_int
+    lib.gemv_fused_ncols.argtypes = [_VP, ctypes.c_int, _I64, _I64, _I64, _VP, ctypes.c_int, _VIEWP, _VIEWP,
+                                     _VIEWP, _VP]
+    lib.gemv_fused_ncols.restype = ctypes.c_int
+    lib.gemv_fused_ncols_validate.argtypes = [_VP, ctypes.c_int, _I64, _I64, _I64, _VP, ctypes.c_int, _VIEWP,
+                                              _VIEWP, _VIEWP]
+    lib.gemv_fused_ncols_validate.restype = ctypes.c_int
     lib.gemv_weight_bytes.argtypes = [ctypes.c_int, _I64, _I64]
     lib.gemv_weight_bytes.restype = _I64
     lib.gemv_strerror.argtypes = [ctypes.c_int]
@@ -192,6 +198,20 @@ def gemv_glu_validate(W_gate, W_up, wfmt, N, K, x, act="silu", dst=None) -> int:
                                     _as_view(dst))
 
 
+def gemv_fused_ncols(W, wfmt, N, K, ncols, x, act, mul_operand=None, add_operand=None, dst=None, stream=None):
+    """dst[b, i] = epilogue((W x_b)_i) for ncols columns x_b = x[b] (x: [ncols, K]
+    f32; dst and operands: ncols * N f32 in [ncols][N] order), one launch."""
+    st = load().gemv_fused_ncols(_addr(W), _fmt(wfmt), N, K, ncols, _addr(x), _act(act), _as_view(mul_operand),
+                                 _as_view(add_operand), _as_view(dst), _stream(stream))
+    if st != 0:
+        _raise(st)
+
+
+def gemv_fused_ncols_validate(W, wfmt, N, K, ncols, x, act, mul_operand=None, add_operand=None, dst=None) -> int:
+    return load().gemv_fused_ncols_validate(_addr(W), _fmt(wfmt), N, K, ncols, _addr(x), _act(act),
+                                            _as_view(mul_operand), _as_view(add_operand), _as_view(dst))
+
+
 def gemv_weight_bytes(wfmt, N, K) -> int:
     return int(load().gemv_weight_bytes(_fmt(wfmt), N, K))
 
@@ -232,5 +252,18 @@ class PreparedCall:
 
     def __call__(self, stream=None):
         st = self._lib.gemv_fused(*self._args, *self._ptrs, _stream(stream))
+        if st != 0:
+            _raise(st)
+
+
+class PreparedNcols(PreparedCall):
+    """A gemv_fused_ncols call with its views marshalled once."""
+
+    def __init__(self, W, wfmt, N, K, ncols, x, act, mul_operand=None, add_operand=None, dst=None):
+        super().__init__(W, wfmt, N, K, x, act, mul_operand, add_operand, dst)
+        self._args = (_addr(W), _fmt(wfmt), N, K, ncols, _addr(x), _act(act))
+
+    def __call__(self, stream=None):
+        st = self._lib.gemv_fused_ncols(*self._args, *self._ptrs, _stream(stream))
         if st != 0:
             _raise(st)

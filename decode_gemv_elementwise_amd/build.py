@@ -8,6 +8,8 @@ hipcc cross-compiles without a GPU.  Flags:
 """
 import os
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -17,7 +19,8 @@ LIB = os.path.join(HERE, "libgemv_fused.so")
 PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = [os.path.join(CSRC, "gemv_kernels.hip"), os.path.join(CSRC, "gemv_validate.cpp")]
+SOURCES = [os.path.join(CSRC, "gemv_kernels.hip"), os.path.join(CSRC, "gemv_cols.hip"),
+           os.path.join(CSRC, "gemv_validate.cpp")]
 PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -25,15 +28,25 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contra
              "-Wall", "-Wno-unused-result"]
 
 
-def _compile(sources, out, verbose, extra_flags=()):
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-shared", "-o", tmp, *sources]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, out)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+
+
+def _compile(sources, out, verbose, extra_flags=()):
+    """Compiles each source to an object (in parallel), then links them."""
+    with tempfile.TemporaryDirectory(prefix="gemv_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, f"{i}_{os.path.basename(src)}.o") for i, src in enumerate(sources)]
+        cmds = [[HIPCC, *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c", "-o", o, src]
+                for src, o in zip(sources, objs)]
+        with ThreadPoolExecutor(max(1, min(len(cmds), 4))) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp = out + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", "-o", tmp, *objs], verbose)
+        os.replace(tmp, out)
     return out
 
 

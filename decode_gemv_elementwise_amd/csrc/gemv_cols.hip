@@ -1,0 +1,445 @@
+// Several destination columns over one weight matrix (ncols = 2..8):
+// dst[b*N + i] = epilogue((W x_b)_i, operand[b*N + i]).
+//
+// "feat(cuda): fuse activations and residual add into mmv f/q epilogues",
+// Summary, states the fused matrix-vector path for one destination column;
+// with a handful of columns (small-batch or speculative decode) W is still
+// the only large operand, so the kernel streams it from HBM once and applies
+// every chunk to all columns.  Each 16-byte chunk is decoded once into
+// registers and then multiplied into the ncols running sums of its row; as
+// ncols grows the work per weight byte grows with it, and the kernel moves
+// from the HBM roof towards the VALU roof.
+//
+// Layout of the work, per workgroup of kWaves waves and a tile of kWaves * R
+// rows (wave w owns rows tile*kWaves*R + w*R + [0, R)):
+//  * K is walked in segments of 64 * U chunks.  A segment of x, for all
+//    columns, is staged in LDS (ncols planes of 64 * U * E floats); the next
+//    segment's x is loaded into registers while the current one is used, and
+//    the next segment's W batch (R rows x U chunks per lane) is in flight
+//    while the current batch is consumed.
+//  * Lane l owns chunks l, l + 64, ... of each row, in the same order as the
+//    one-column kernel, and the row sums are reduced with the same wave
+//    reduction: column b of the result is bit for bit the one-column result.
+//  * LDS holds each plane without padding; the 16-byte pieces of a chunk are
+//    permuted by an XOR of the chunk index so that the 16-byte reads of 8 (or
+//    16) consecutive lanes fall in distinct bank groups.
+//  * Lane j < R * ncols finishes output (row R-block j % R, column j / R):
+//    consecutive lanes store consecutive rows of one column.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <mutex>
+
+#include "gemv_device.h"
+#include "gemv_internal.h"
+
+namespace gemv {
+namespace {
+
+// Tuning: waves per workgroup, the x-staging budget that sets the segment
+// length, and the chunk loads per lane a batch aims for.
+#ifndef GEMV_COLS_WAVES
+#define GEMV_COLS_WAVES 4
+#endif
+#ifndef GEMV_COLS_X_BUDGET
+#define GEMV_COLS_X_BUDGET 64
+#endif
+#ifndef GEMV_COLS_LOADS
+#define GEMV_COLS_LOADS 8
+#endif
+#ifndef GEMV_COLS_SERIAL
+#define GEMV_COLS_SERIAL 1
+#endif
+
+template <int FMT, int NC> struct ColsCfg {
+    static constexpr int E = Fmt<FMT>::E;
+    static constexpr int kWaves = GEMV_COLS_WAVES;
+    // chunks per lane per segment: GEMV_COLS_X_BUDGET / (NC * E), 1..8 (a
+    // short segment keeps the LDS per workgroup small and occupancy up)
+    static constexpr int kU0 = GEMV_COLS_X_BUDGET / (NC * E);
+    static constexpr int U = kU0 < 1 ? 1 : (kU0 > 8 ? 8 : kU0);
+    // rows per wave: about GEMV_COLS_LOADS chunk loads per lane per batch, 1..4
+    static constexpr int kR0 = GEMV_COLS_LOADS / U;
+    static constexpr int R = kR0 > 4 ? 4 : (kR0 < 1 ? 1 : kR0);
+    static constexpr int SEG = 64 * U * E;     // x floats per column per segment
+    static constexpr int kPlane4 = SEG / 4;    // float4 slots per plane (a multiple of 64)
+    static constexpr int kBuf4 = NC * kPlane4; // float4 slots per segment buffer
+    static constexpr int kCopies = kBuf4 / kWave;                // 64-slot wave copies per segment
+    static constexpr int kDma = (kCopies + kWaves - 1) / kWaves; // copies per wave (the last may be idle)
+};
+
+// Physical float4 slot of float4 f of a plane: the E/4 pieces of chunk
+// c = f / (E/4) are permuted by an XOR with bits of c, so that for any 8 (or
+// 16) consecutive chunks read by consecutive lanes the same piece lands in 8
+// (or 16) distinct 16-byte bank groups.
+template <int FMT> __device__ __forceinline__ int swz(int f)
+{
+    constexpr int P = Fmt<FMT>::E / 4;        // pieces per chunk: 1, 2, 4 or 8
+    constexpr int e = P == 1 ? 0 : (P == 2 ? 1 : (P == 4 ? 2 : 3));
+    const int c = f >> e;
+    return f ^ (((c >> (3 - e)) ^ (c >> (4 - e))) & (P - 1));
+}
+
+// Copies segment seg of x (all columns) from global memory straight into an
+// LDS buffer (global_load_lds): a wave's 16-byte copy fills 64 consecutive
+// float4 slots, lane i slot p0 + i, so lane i fetches the float4 whose
+// swizzled slot is p0 + i (the swizzle is its own inverse).  When x is not
+// 16-byte aligned the same slots are filled by 4-byte copies, 16 slots per
+// instruction.  Elements past K fetch a clamped, valid address; those slots
+// belong to chunks past the end of the row and are never used.
+template <int FMT, int NC>
+__device__ __forceinline__ void dma_x_segment(f32x4 *buf, const float *x, int K, int seg, int wave, int lane,
+                                              bool aligned16)
+{
+    using C = ColsCfg<FMT, NC>;
+    const int k4 = K / 4; // K is a multiple of 4 on this path
+    if (aligned16) {
+#pragma unroll
+        for (int j = 0; j < C::kDma; ++j) {
+            const int copy = wave + C::kWaves * j; // wave-uniform
+            if (C::kCopies % C::kWaves != 0 && copy >= C::kCopies)
+                break;
+            const int p0 = kWave * copy;           // first slot of this copy
+            const int b = p0 / C::kPlane4;         // a copy never straddles planes
+            const int f = swz<FMT>(p0 % C::kPlane4 + lane);
+            const int g = min(seg * C::kPlane4 + f, k4 - 1);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(x + (int64_t)b * K + 4 * g),
+                                             (__attribute__((address_space(3))) void *)(buf + p0), 16, 0, 0);
+        }
+    } else {
+        float *bufd = reinterpret_cast<float *>(buf);
+#pragma unroll
+        for (int j = 0; j < 4 * C::kDma; ++j) {
+            const int copy = wave + C::kWaves * j; // 64-dword copies, wave-uniform
+            if (copy >= 4 * C::kCopies)
+                break;
+            const int d = kWave * copy + lane;     // dword slot of this lane
+            const int p = d / 4;
+            const int b = p / C::kPlane4;
+            const int f = swz<FMT>(p % C::kPlane4);
+            const int g = min(seg * C::kPlane4 + f, k4 - 1);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(x + (int64_t)b * K + 4 * g + d % 4),
+                                             (__attribute__((address_space(3))) void *)(bufd + kWave * copy), 4,
+                                             0, 0);
+        }
+    }
+}
+
+template <int FMT, int NC, int R, int U>
+__device__ __forceinline__ void consume_cols(const Batch<FMT, R, U> &b, const f32x4 *xs, float (&acc)[R][NC],
+                                             int lane, int chunk0, int nchunks)
+{
+    using F = Fmt<FMT>;
+    constexpr int P = F::E / 4;
+    constexpr int kPlane4 = ColsCfg<FMT, NC>::kPlane4;
+    const f32x4 *xs4 = xs;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int cl = lane + kWave * u; // chunk within the segment
+        const bool valid = chunk0 + cl < nchunks;
+        typename F::Dq dq[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            dq[r] = F::decode(b.q[r][u]);
+#pragma unroll
+        for (int col = 0; col < NC; ++col) {
+            float xv[F::E];
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                const f32x4 t = xs4[col * kPlane4 + swz<FMT>(cl * P + i)];
+                xv[4 * i] = t.x;
+                xv[4 * i + 1] = t.y;
+                xv[4 * i + 2] = t.z;
+                xv[4 * i + 3] = t.w;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float t;
+                if constexpr (F::kBlock)
+                    t = F::dotd(dq[r], xv, b.sc[r][u], acc[r][col]);
+                else
+                    t = F::dotd(dq[r], xv, acc[r][col]);
+                acc[r][col] = valid ? t : acc[r][col];
+            }
+#if GEMV_COLS_SERIAL
+            // one column at a time: hoisting the x reads of every column ahead
+            // of the FMAs would hold U * NC * E floats in registers
+            __builtin_amdgcn_sched_barrier(0);
+#endif
+        }
+    }
+}
+
+template <int FMT, int NC>
+__global__ __launch_bounds__((ColsCfg<FMT, NC>::kWaves * kWave)) void gemv_cols_kernel(
+    const unsigned char *__restrict__ W, const float *__restrict__ x, int N, int K, int act, const float *mop,
+    const float *rop, float *dst)
+{
+    using F = Fmt<FMT>;
+    using C = ColsCfg<FMT, NC>;
+    constexpr int R = C::R, U = C::U, SEGC = kWave * C::U;
+    // two segment buffers (x of segment s+1 lands in one while segment s is
+    // read from the other); a row of one segment gets only the first
+    extern __shared__ f32x4 lds4[];
+    f32x4 *const xa = lds4;
+    f32x4 *const xb = lds4 + C::kBuf4;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nchunks = K / F::E;
+    const int nseg = (nchunks + SEGC - 1) / SEGC;
+    const int row0 = (blockIdx.x * C::kWaves + wave) * R;
+    const int64_t rbytes = row_bytes<FMT>(K);
+    const unsigned char *scales = F::kBlock ? W + align256_dev((int64_t)N * rbytes) : nullptr;
+    const int64_t sbytes = (int64_t)(K / 32) * 2;
+
+    // 1. epilogue operand of the output this lane finishes (lane j: row
+    //    row0 + j % R of column j / R; other lanes read a clamped element)
+    const int jo = min(lane, R * NC - 1);
+    const int orow = min(row0 + jo % R, N - 1), ocol = jo / R;
+    const bool has_op = act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL || act == GEMV_ACT_ADD;
+    const float *opp = act == GEMV_ACT_ADD ? rop : (has_op ? mop : x);
+    const float opv = opp[has_op ? (int64_t)ocol * N + orow : 0];
+
+    // 2. x of the first segment, straight into LDS
+    const bool x16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    dma_x_segment<FMT, NC>(xa, x, K, 0, wave, lane, x16);
+
+    // 3. W, first batch
+    const unsigned char *wrow[R];
+    const unsigned char *srow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = min(row0 + r, N - 1);
+        wrow[r] = W + (int64_t)row * rbytes;
+        srow[r] = F::kBlock ? scales + (int64_t)row * sbytes : nullptr;
+    }
+    Batch<FMT, R, U> b0, b1;
+    issue_batch<FMT, R, U>(b0, wrow, srow, lane, 0, nchunks);
+
+    float acc[R][NC];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            acc[r][c] = 0.0f;
+
+    // 4. segments, two per trip: even segments use buffer xa and batch b0, odd
+    //    ones xb and b1.  At the top of a segment this wave's only outstanding
+    //    loads are that segment's x copy and W batch, both needed now, so it
+    //    waits for all of them; the barrier then makes every wave's copy
+    //    visible and guarantees that all waves are done with the other buffer,
+    //    which the next segment's copy overwrites.
+    for (int s = 0;;) {
+        __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0); expcnt, lgkmcnt not waited for
+        __builtin_amdgcn_s_barrier();
+        if (s + 1 < nseg) {
+            dma_x_segment<FMT, NC>(xb, x, K, s + 1, wave, lane, x16);
+            issue_batch<FMT, R, U>(b1, wrow, srow, lane, (s + 1) * U, nchunks);
+        }
+        consume_cols<FMT, NC, R, U>(b0, xa, acc, lane, s * SEGC, nchunks);
+        if (++s == nseg)
+            break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_s_barrier();
+        if (s + 1 < nseg) {
+            dma_x_segment<FMT, NC>(xa, x, K, s + 1, wave, lane, x16);
+            issue_batch<FMT, R, U>(b0, wrow, srow, lane, (s + 1) * U, nchunks);
+        }
+        consume_cols<FMT, NC, R, U>(b1, xb, acc, lane, s * SEGC, nchunks);
+        if (++s == nseg)
+            break;
+    }
+
+    // 5. reduce every (row, column) sum; lane j takes output j
+    float mine = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float sum = wave_sum(acc[r][c]);
+            mine = lane == c * R + r ? sum : mine;
+        }
+    const float y = apply_epilogue(act, mine, opv);
+    if (lane < R * NC && row0 + lane % R < N)
+        dst[(int64_t)(lane / R) * N + row0 + lane % R] = y;
+}
+
+// Any K (float formats whose rows are not whole 16-byte chunks, or x too long
+// for the one-column kernel's LDS): one wave per row, element loads, x read
+// through the caches, in the order of the one-column generic kernel.
+template <int FMT>
+__device__ __forceinline__ float weight_at_cols(const unsigned char *W, int N, int K, int row, int k)
+{
+    if constexpr (FMT == GEMV_W_F32) {
+        return reinterpret_cast<const float *>(W)[(int64_t)row * K + k];
+    } else if constexpr (FMT == GEMV_W_F16) {
+        return (float)reinterpret_cast<const _Float16 *>(W)[(int64_t)row * K + k];
+    } else if constexpr (FMT == GEMV_W_BF16) {
+        unsigned short b = reinterpret_cast<const unsigned short *>(W)[(int64_t)row * K + k];
+        return __builtin_bit_cast(float, (unsigned)b << 16);
+    } else if constexpr (FMT == GEMV_W_Q8B32) {
+        const unsigned char *scales = W + align256_dev((int64_t)N * K);
+        float s = load_scale(scales + ((int64_t)row * (K / 32) + k / 32) * 2);
+        return (float)(int)(signed char)W[(int64_t)row * K + k] * s;
+    } else {
+        const unsigned char *scales = W + align256_dev((int64_t)N * K / 2);
+        float s = load_scale(scales + ((int64_t)row * (K / 32) + k / 32) * 2);
+        unsigned char b = W[(int64_t)row * (K / 2) + k / 2];
+        int c = (k & 1) ? (b >> 4) : (b & 0xF);
+        return (float)(c - 8) * s;
+    }
+}
+
+template <int FMT, int NC>
+__global__ __launch_bounds__(256) void gemv_cols_generic_kernel(const unsigned char *__restrict__ W,
+                                                                const float *__restrict__ x, int N, int K, int act,
+                                                                const float *mop, const float *rop, float *dst)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nwaves = gridDim.x * (blockDim.x / kWave);
+    for (int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; row < N; row += nwaves) {
+        float acc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            acc[c] = 0.0f;
+        for (int k = lane; k < K; k += kWave) {
+            const float w = weight_at_cols<FMT>(W, N, K, row, k);
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                acc[c] = fmaf(w, x[(int64_t)c * K + k], acc[c]);
+        }
+        float mine = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float sum = wave_sum(acc[c]);
+            mine = lane == c ? sum : mine;
+        }
+        if (lane < NC) {
+            const int64_t o = (int64_t)lane * N + row;
+            const bool has_op = act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL || act == GEMV_ACT_ADD;
+            const float v = has_op ? (act == GEMV_ACT_ADD ? rop[o] : mop[o]) : 0.0f;
+            dst[o] = apply_epilogue(act, mine, v);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host dispatch
+
+struct ColsCall {
+    const unsigned char *W;
+    const float *x;
+    int N, K, act;
+    const float *m, *r;
+    float *dst;
+};
+
+template <int FMT, int NC> hipError_t launch_cols(const ColsCall &c, hipStream_t s)
+{
+    using C = ColsCfg<FMT, NC>;
+    const void *fn = reinterpret_cast<const void *>(&gemv_cols_kernel<FMT, NC>);
+    const int nchunks = c.K / C::E;
+    const int nseg = (nchunks + kWave * C::U - 1) / (kWave * C::U);
+    const size_t lds = (size_t)(nseg > 1 ? 2 : 1) * C::kBuf4 * 16;
+    if (2 * C::kBuf4 * 16 > 64 * 1024) {
+        static std::once_flag once;
+        static hipError_t attr_err = hipSuccess;
+        std::call_once(once, [&] { attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds); });
+        if (attr_err != hipSuccess)
+            return attr_err;
+    }
+    const int rows_per_tile = C::kWaves * C::R;
+    const int grid = (c.N + rows_per_tile - 1) / rows_per_tile;
+    const unsigned char *W = c.W;
+    const float *x = c.x;
+    int N = c.N, K = c.K, act = c.act;
+    const float *m = c.m, *r = c.r;
+    float *dst = c.dst;
+    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst};
+    return hipLaunchKernel(fn, dim3(grid), dim3(C::kWaves * kWave), args, lds, s);
+}
+
+template <int FMT, int NC> hipError_t launch_cols_generic(const ColsCall &c, hipStream_t s)
+{
+    const void *fn = reinterpret_cast<const void *>(&gemv_cols_generic_kernel<FMT, NC>);
+    int grid = (c.N + 3) / 4;
+    if (grid > 65536)
+        grid = 65536;
+    const unsigned char *W = c.W;
+    const float *x = c.x;
+    int N = c.N, K = c.K, act = c.act;
+    const float *m = c.m, *r = c.r;
+    float *dst = c.dst;
+    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst};
+    return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, s);
+}
+
+// The chunked kernel exactly where the one-column call takes its chunked
+// kernel (rows of whole 16-byte chunks, x of one column fits the one-column
+// kernel's padded LDS staging), so that every column reduces in the same
+// order as the one-column call.
+template <int FMT, int NC> hipError_t dispatch_cols(const ColsCall &c, hipStream_t s)
+{
+    const int64_t lds1 = (int64_t)(c.K / Fmt<FMT>::E) * Fmt<FMT>::XS * 4;
+    const bool fast = (row_bytes<FMT>(c.K) % 16 == 0) && lds1 <= kMaxLds;
+    return fast ? launch_cols<FMT, NC>(c, s) : launch_cols_generic<FMT, NC>(c, s);
+}
+
+template <int NC> hipError_t dispatch_cols_fmt(int wfmt, const ColsCall &c, hipStream_t s)
+{
+    switch (wfmt) {
+    case GEMV_W_F32:
+        return dispatch_cols<GEMV_W_F32, NC>(c, s);
+    case GEMV_W_F16:
+        return dispatch_cols<GEMV_W_F16, NC>(c, s);
+    case GEMV_W_BF16:
+        return dispatch_cols<GEMV_W_BF16, NC>(c, s);
+    case GEMV_W_Q8B32:
+        return dispatch_cols<GEMV_W_Q8B32, NC>(c, s);
+    default:
+        return dispatch_cols<GEMV_W_Q4B32, NC>(c, s);
+    }
+}
+
+hipError_t dispatch_ncols(int wfmt, int ncols, const ColsCall &c, hipStream_t s)
+{
+    switch (ncols) {
+    case 2:
+        return dispatch_cols_fmt<2>(wfmt, c, s);
+    case 3:
+        return dispatch_cols_fmt<3>(wfmt, c, s);
+    case 4:
+        return dispatch_cols_fmt<4>(wfmt, c, s);
+    case 5:
+        return dispatch_cols_fmt<5>(wfmt, c, s);
+    case 6:
+        return dispatch_cols_fmt<6>(wfmt, c, s);
+    case 7:
+        return dispatch_cols_fmt<7>(wfmt, c, s);
+    default:
+        return dispatch_cols_fmt<8>(wfmt, c, s);
+    }
+}
+
+} // namespace
+} // namespace gemv
+
+extern "C" {
+
+int gemv_fused_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
+                     const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst,
+                     void *hip_stream)
+{
+    int st = gemv::validate_ncols(W, wfmt, N, K, ncols, x, act, mul_operand, add_operand, dst);
+    if (st != GEMV_OK)
+        return st;
+    if (ncols == 1)
+        return gemv_fused(W, wfmt, N, K, x, act, mul_operand, add_operand, dst, hip_stream);
+    gemv::ColsCall c{static_cast<const unsigned char *>(W), x, (int)N, (int)K, act,
+                     mul_operand ? mul_operand->data : nullptr, add_operand ? add_operand->data : nullptr,
+                     dst->data};
+    return gemv::finish_launch(
+        (int)gemv::dispatch_ncols(wfmt, (int)ncols, c, static_cast<hipStream_t>(hip_stream)));
+}
+
+} // extern "C"

@@ -18,5 +18,12 @@ int validate_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul
 int validate_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,
                  const gemv_view *dst);
 const char *strerror_of(int status);
+int validate_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
+                   const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst);
+
+// Records a launch's hipError_t as the calling thread's last HIP error and
+// maps it to GEMV_OK or GEMV_E_HIP.
+int finish_launch(int hip_error);
+int last_hip_error();
 
 } // namespace gemv

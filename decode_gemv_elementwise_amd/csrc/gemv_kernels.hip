@@ -35,234 +35,11 @@
 #include <cstdint>
 #include <mutex>
 
+#include "gemv_device.h"
 #include "gemv_internal.h"
 
 namespace gemv {
 namespace {
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kWave = 64;
-__host__ __device__ __forceinline__ int64_t align256_dev(int64_t v) { return (v + 255) / 256 * 256; }
-constexpr int kMaxLds = 160 * 1024; // LDS bytes a gfx950 workgroup may allocate
-
-// ------------------------------------------------------------------ epilogue
-
-// sigmoid(a) = 1 / (1 + e^-a) and silu(a) = a * sigmoid(a), evaluated with
-// t = e^-|a| <= 1 so that nothing overflows: for a < 0 the same values are
-// t / (1 + t) and a t / (1 + t).  (The direct form turns silu(a) into -0 once
-// e^-a overflows, near a = -88.7, although the true value is still a normal
-// float there.)
-__device__ __forceinline__ float sigmoid_f(float a)
-{
-    float t = expf(-fabsf(a));
-    return (a >= 0.0f ? 1.0f : t) / (1.0f + t);
-}
-
-__device__ __forceinline__ float silu_f(float a)
-{
-    float t = expf(-fabsf(a));
-    return (a >= 0.0f ? a : a * t) / (1.0f + t);
-}
-
-// The epilogue of one output: v is m_i for SILU_MUL and MUL, r_i for ADD.
-__device__ __forceinline__ float apply_epilogue(int act, float a, float v)
-{
-    switch (act) {
-    case GEMV_ACT_SIGMOID:
-        return sigmoid_f(a);
-    case GEMV_ACT_SILU:
-        return silu_f(a);
-    case GEMV_ACT_SILU_MUL: {
-        float s = silu_f(a);
-        return s * v;
-    }
-    case GEMV_ACT_MUL:
-        return a * v;
-    case GEMV_ACT_ADD:
-        return a + v;
-    default:
-        return a;
-    }
-}
-
-__device__ __forceinline__ float operand_of(int act, const float *m, const float *r, int64_t i)
-{
-    if (act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL)
-        return m[i];
-    if (act == GEMV_ACT_ADD)
-        return r[i];
-    return 0.0f;
-}
-
-// ------------------------------------------------------------------ wave reduce
-
-// A DPP lane permutation of v.  Every pattern used below reads a valid lane,
-// so bound_ctrl is irrelevant to the result; setting it lets the compiler
-// fold the move into the consuming add (v_add_f32_dpp).
-template <int CTRL> __device__ __forceinline__ float dpp(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-__device__ __forceinline__ float lane_read(float v, int l)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-
-// Sum of v over the 64 lanes, returned uniformly.  quad_perm swaps, then
-// half-row and row mirrors leave each 16-lane row's sum in all its lanes.
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v); // row_half_mirror
-    v += dpp<0x140>(v); // row_mirror
-    return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
-}
-
-// ------------------------------------------------------------------ formats
-// E:   weights per 16-byte chunk of W.
-// XS:  LDS floats per chunk of x (E plus padding).
-// kBlock: the format has an fp16 scale plane; a chunk is 1/kChunksPerBlock
-//         of a 32-weight block.
-
-__device__ __forceinline__ float f16lo(unsigned d) { return (float)__builtin_bit_cast(f16x2, d).x; }
-__device__ __forceinline__ float f16hi(unsigned d) { return (float)__builtin_bit_cast(f16x2, d).y; }
-
-template <int FMT> struct Fmt;
-
-template <> struct Fmt<GEMV_W_F32> {
-    static constexpr int E = 4, XS = 4;
-    static constexpr bool kBlock = false;
-    static constexpr int kChunksPerBlock = 0;
-    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float acc)
-    {
-        // Copy the lanes out before reinterpreting: __builtin_bit_cast applied
-        // to an element of an ext_vector_type reads the vector's first element.
-        unsigned d[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc = fmaf(__builtin_bit_cast(float, d[i]), xv[i], acc);
-        return acc;
-    }
-};
-
-template <> struct Fmt<GEMV_W_F16> {
-    static constexpr int E = 8, XS = 12;
-    static constexpr bool kBlock = false;
-    static constexpr int kChunksPerBlock = 0;
-    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float acc)
-    {
-        unsigned d[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = fmaf(f16lo(d[i]), xv[2 * i], acc);
-            acc = fmaf(f16hi(d[i]), xv[2 * i + 1], acc);
-        }
-        return acc;
-    }
-};
-
-template <> struct Fmt<GEMV_W_BF16> {
-    static constexpr int E = 8, XS = 12;
-    static constexpr bool kBlock = false;
-    static constexpr int kChunksPerBlock = 0;
-    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float acc)
-    {
-        unsigned d[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = fmaf(__builtin_bit_cast(float, d[i] << 16), xv[2 * i], acc);
-            acc = fmaf(__builtin_bit_cast(float, d[i] & 0xFFFF0000u), xv[2 * i + 1], acc);
-        }
-        return acc;
-    }
-};
-
-// 8-bit blocks: a chunk is 16 codes (half a block).  Partial sum of code * x,
-// then one multiply-add by the block scale.
-template <> struct Fmt<GEMV_W_Q8B32> {
-    static constexpr int E = 16, XS = 20;
-    static constexpr bool kBlock = true;
-    static constexpr int kChunksPerBlock = 2;
-    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float scale, float acc)
-    {
-        unsigned d[4] = {q.x, q.y, q.z, q.w};
-        float p = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                float w = (float)(int)(signed char)((d[i] >> (8 * b)) & 0xFF);
-                p = fmaf(w, xv[4 * i + b], p);
-            }
-        }
-        return fmaf(p, scale, acc);
-    }
-};
-
-// (d & mask) | bits in one VALU op.  The compiler emits an AND and an OR with
-// literal operands; v_and_or_b32 takes one constant from an SGPR and the other
-// from a VGPR (gfx9 VOP3 reads at most one scalar operand).
-__device__ __forceinline__ unsigned and_or(unsigned d, unsigned mask, unsigned bits)
-{
-    unsigned r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(d), "s"(mask), "v"(bits));
-    return r;
-}
-
-// 4-bit blocks: a chunk is one whole block of 32 codes.  A dword holds
-// elements 8i..8i+7, element k in bits 4k..4k+3.  OR-ing a nibble into the
-// mantissa of the f16 constant 1024 gives 1024 + c exactly (nibble at bit 0)
-// or 1024 + 16c (nibble at bit 4); subtracting 1032 or 1152 leaves c - 8 or
-// 16 (c - 8) exactly, as a packed f16 pair.  The 16x lane is folded back with
-// an exact multiply by 1/16 once per block.
-template <> struct Fmt<GEMV_W_Q4B32> {
-    static constexpr int E = 32, XS = 36;
-    static constexpr bool kBlock = true;
-    static constexpr int kChunksPerBlock = 1;
-    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float scale, float acc)
-    {
-        const f16x2 off1 = {(_Float16)1032.0f, (_Float16)1032.0f};
-        const f16x2 off16 = {(_Float16)1152.0f, (_Float16)1152.0f};
-        const unsigned magic = 0x64006400u;
-        unsigned d[4] = {q.x, q.y, q.z, q.w};
-        float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float *xi = xv + 8 * i;
-            const unsigned e = d[i] >> 8;
-            f16x2 h0 = __builtin_bit_cast(f16x2, and_or(d[i], 0x000F000Fu, magic)) - off1;  // c0-8, c4-8
-            f16x2 h1 = __builtin_bit_cast(f16x2, and_or(d[i], 0x00F000F0u, magic)) - off16; // 16(c1-8), 16(c5-8)
-            f16x2 h2 = __builtin_bit_cast(f16x2, and_or(e, 0x000F000Fu, magic)) - off1;     // c2-8, c6-8
-            f16x2 h3 = __builtin_bit_cast(f16x2, and_or(e, 0x00F000F0u, magic)) - off16;    // 16(c3-8), 16(c7-8)
-            a0 = fmaf((float)h0.x, xi[0], a0);
-            a0 = fmaf((float)h0.y, xi[4], a0);
-            a0 = fmaf((float)h2.x, xi[2], a0);
-            a0 = fmaf((float)h2.y, xi[6], a0);
-            a1 = fmaf((float)h1.x, xi[1], a1);
-            a1 = fmaf((float)h1.y, xi[5], a1);
-            a1 = fmaf((float)h3.x, xi[3], a1);
-            a1 = fmaf((float)h3.y, xi[7], a1);
-        }
-        return fmaf(fmaf(a1, 0.0625f, a0), scale, acc);
-    }
-};
-
-// Byte layout helpers (see the header for the formats).
-template <int FMT> __host__ __device__ __forceinline__ int64_t row_bytes(int64_t K)
-{
-    return FMT == GEMV_W_F32 ? K * 4 : (FMT == GEMV_W_Q8B32 ? K : (FMT == GEMV_W_Q4B32 ? K / 2 : K * 2));
-}
-
-__device__ __forceinline__ float load_scale(const unsigned char *p)
-{
-    unsigned short h = *reinterpret_cast<const unsigned short *>(p);
-    return (float)__builtin_bit_cast(_Float16, h);
-}
 
 // ------------------------------------------------------------------ fast kernel
 // Requires: W 16-byte aligned, row_bytes(K) % 16 == 0, (K / E) * XS * 4 bytes
@@ -282,27 +59,6 @@ __device__ __forceinline__ float load_scale(const unsigned char *p)
 // hardware's load counter retires in order: waiting for x then does not wait
 // for W, and the barrier after staging waits only for LDS.
 
-template <int FMT, int R, int U> struct Batch {
-    u32x4 q[R][U];
-    float sc[R][U];
-};
-
-template <int FMT, int R, int U>
-__device__ __forceinline__ void issue_batch(Batch<FMT, R, U> &b, const unsigned char *const *wrow,
-                                            const unsigned char *const *srow, int lane, int jb, int nchunks)
-{
-    using F = Fmt<FMT>;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = min(lane + kWave * (jb + u), nchunks - 1);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            b.q[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[r]) + c);
-            if constexpr (F::kBlock)
-                b.sc[r][u] = load_scale(srow[r] + 2 * (c / F::kChunksPerBlock));
-        }
-    }
-}
 
 template <int FMT, int R, int U>
 __device__ __forceinline__ void consume_batch(const Batch<FMT, R, U> &b, const float *xs, float *acc, int lane,
@@ -377,14 +133,6 @@ template <int FMT, int kStage> struct XStage {
     }
 };
 
-// Workgroup barrier for LDS only: waits for this wave's LDS writes, not for
-// its outstanding global loads.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Optional occupancy floor (waves per SIMD) for the register allocator; 0 = none.
 #ifndef GEMV_MIN_WAVES_PER_SIMD
@@ -395,14 +143,6 @@ template <int WAVES> constexpr int min_blocks_per_cu()
     return GEMV_MIN_WAVES_PER_SIMD > 0 ? (GEMV_MIN_WAVES_PER_SIMD * 4 + WAVES - 1) / WAVES : 1;
 }
 
-// The gated pair of products (GLU): W is the gate matrix and W2 the up matrix,
-// both streamed over the same staged x; the wave's batch holds R gate rows
-// followed by the same R up rows, and the epilogue is act(gate) * up.
-__device__ __forceinline__ float apply_glu(int act, float g, float u)
-{
-    const float a = act == GEMV_ACT_SIGMOID ? sigmoid_f(g) : silu_f(g);
-    return a * u;
-}
 
 template <int FMT, int WAVES, int R, int U, bool MULTI, bool GLU>
 __global__ __launch_bounds__(WAVES *kWave, min_blocks_per_cu<WAVES>()) void gemv_fast_kernel(const unsigned char *__restrict__ W,
@@ -579,8 +319,6 @@ __global__ __launch_bounds__(256) void gemv_epilogue_kernel(int N, const float *
 
 // ------------------------------------------------------------------ host dispatch
 
-thread_local int t_last_hip_error = 0;
-
 struct Call {
     const unsigned char *W;
     const unsigned char *W2; // up matrix of a gated pair, else nullptr
@@ -714,13 +452,22 @@ template <bool GLU> hipError_t dispatch_any(int wfmt, const Call &c, hipStream_t
     }
 }
 
-int finish(hipError_t e)
-{
-    t_last_hip_error = (int)e;
-    return e == hipSuccess ? GEMV_OK : GEMV_E_HIP;
-}
+int finish(hipError_t e) { return finish_launch((int)e); }
 
 } // namespace
+
+namespace {
+thread_local int t_last_hip_error = 0;
+}
+
+int finish_launch(int hip_error)
+{
+    t_last_hip_error = hip_error;
+    return hip_error == (int)hipSuccess ? GEMV_OK : GEMV_E_HIP;
+}
+
+int last_hip_error() { return t_last_hip_error; }
+
 } // namespace gemv
 
 extern "C" {
@@ -764,6 +511,6 @@ int gemv_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul_ope
     return gemv::finish(e);
 }
 
-int gemv_last_hip_error(void) { return gemv::t_last_hip_error; }
+int gemv_last_hip_error(void) { return gemv::last_hip_error(); }
 
 } // extern "C"

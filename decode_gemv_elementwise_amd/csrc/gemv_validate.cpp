@@ -133,8 +133,8 @@ int check_epilogue_views(int act, int64_t N, const gemv_view *mul_operand, const
 
 } // namespace
 
-int validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int act,
-             const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst)
+int validate_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
+                   const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst)
 {
     if (!W || !x)
         return GEMV_E_NULL;
@@ -143,12 +143,17 @@ int validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int 
     int st = check_act(act);
     if (st != GEMV_OK)
         return st;
+    if (ncols < 1 || ncols > GEMV_MAX_NCOLS)
+        return GEMV_E_DIM;
     int64_t wbytes = weight_bytes(wfmt, N, K);
     if (wbytes < 0)
         return static_cast<int>(wbytes);
+    const int64_t nout = N * ncols; // N < 2^31 and ncols <= 8: no overflow
+    if (nout >= GEMV_MAX_DIM_EXTENT)
+        return GEMV_E_DIM;
 
     const gemv_view *operand = nullptr;
-    st = check_epilogue_views(act, N, mul_operand, add_operand, dst, &operand);
+    st = check_epilogue_views(act, nout, mul_operand, add_operand, dst, &operand);
     if (st != GEMV_OK)
         return st;
     if (!aligned(W, 16) || !aligned(x, 4))
@@ -156,12 +161,18 @@ int validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int 
 
     // dst never overlaps the matmul inputs; it overlaps the operand only as
     // the identical view (same pointer; shapes are equal and both contiguous).
-    Span sd = span_of(dst->data, N * 4);
-    if (overlap(sd, span_of(W, wbytes)) || overlap(sd, span_of(x, K * 4)))
+    Span sd = span_of(dst->data, nout * 4);
+    if (overlap(sd, span_of(W, wbytes)) || overlap(sd, span_of(x, ncols * K * 4)))
         return GEMV_E_ALIAS;
-    if (operand && overlap(sd, span_of(operand->data, N * 4)) && operand->data != dst->data)
+    if (operand && overlap(sd, span_of(operand->data, nout * 4)) && operand->data != dst->data)
         return GEMV_E_ALIAS;
     return GEMV_OK;
+}
+
+int validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int act,
+             const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst)
+{
+    return validate_ncols(W, wfmt, N, K, 1, x, act, mul_operand, add_operand, dst);
 }
 
 // The gated pair: both matrices of one format and shape, the gate act SILU
@@ -225,7 +236,7 @@ const char *strerror_of(int status)
         return "a required pointer is NULL";
     case GEMV_E_DIM:
         return "invalid dimensions (N, K < 1 or too large, K not a multiple of 32 for a block "
-               "format, or dst does not hold N elements)";
+               "format, ncols outside 1..8, or dst does not hold ncols * N elements)";
     case GEMV_E_FMT:
         return "unknown weight format";
     case GEMV_E_ACT:
@@ -253,6 +264,12 @@ int gemv_validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x,
                   const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst)
 {
     return gemv::validate(W, wfmt, N, K, x, act, mul_operand, add_operand, dst);
+}
+
+int gemv_fused_ncols_validate(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
+                              const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst)
+{
+    return gemv::validate_ncols(W, wfmt, N, K, ncols, x, act, mul_operand, add_operand, dst);
 }
 
 int gemv_epilogue_validate(int act, int64_t N, const float *acc, const gemv_view *mul_operand,

@@ -22,6 +22,9 @@ Workloads (the decode shapes of a dense 4096-hidden / 14336-FFN layer):
   output), 4096->32 sigmoid.
 * ``q4b32_decode_layer_glu``: the same layer with gate and up as one gated
   pair, silu(W_gate x) * (W_up x) (five calls).
+* ``f16_outproj_residual_4096_ncols8``, ``q4b32_gate_14336x4096_ncols4``:
+  several destination columns over one W (x [ncols, K], operands and dst
+  [ncols, N]).
 
 Draw order per workload, one ``numpy.random.default_rng(seed)`` each: weights
 (codes, then scales) in call order, then x, then m, then r.  Floats are drawn
@@ -150,6 +153,7 @@ class Call:
     out_shape: Optional[Tuple[int, ...]] = None  # view shape of dst (default [N])
     inplace: bool = False  # dst is the same memory as the add/mul operand
     w2: Optional[str] = None  # up matrix of a gated pair: dst = act(w x) * (w2 x)
+    ncols: int = 1  # destination columns: x is [ncols, K], dst and operands [ncols, N]
 
 
 @dataclass
@@ -233,6 +237,28 @@ def q4b32_decode_layer_glu(seed: int = 0) -> Workload:
                     "the 4-bit decode layer with gate and up as one gated pair")
 
 
+def f16_outproj_residual_4096_ncols8(seed: int = 0) -> Workload:
+    """The f16 4096x4096 residual projection over eight destination columns
+    (small-batch decode): x [8, 4096], residual [8, 4096], dst = W x_b + r_b in
+    place."""
+    rng = np.random.default_rng(seed)
+    W = draw_float_weights(rng, "f16", 4096, 4096, 1.0 / 4096)
+    x, r = draw_vec(rng, 8 * 4096), draw_vec(rng, 8 * 4096)
+    calls = [Call("f16_outproj_add_inplace_ncols8", "W", "x", "add", r="r", inplace=True, ncols=8)]
+    return Workload("f16_outproj_residual_4096_ncols8", {"W": W}, {"x": x, "r": r}, calls,
+                    "W 4096x4096 f16 ~N(0,1/4096); eight columns, dst = W x_b + r_b in place")
+
+
+def q4b32_gate_14336x4096_ncols4(seed: int = 0) -> Workload:
+    """The 4-bit 4096->14336 silu gate over four destination columns."""
+    rng = np.random.default_rng(seed)
+    W = draw_q4b32(rng, 14336, 4096, 0.001, 0.02)
+    x = draw_vec(rng, 4 * 4096)
+    calls = [Call("q4_gate_silu_ncols4", "W", "x", "silu", ncols=4)]
+    return Workload("q4b32_gate_14336x4096_ncols4", {"W": W}, {"x": x}, calls,
+                    "4-bit 14336x4096 silu over four columns")
+
+
 WORKLOADS = {
     "f32_tiny_256": f32_tiny_256,
     "f16_outproj_residual_4096": f16_outproj_residual_4096,
@@ -240,6 +266,8 @@ WORKLOADS = {
     "q8b32_view_residual_4096x6144": q8b32_view_residual_4096x6144,
     "q4b32_decode_layer": q4b32_decode_layer,
     "q4b32_decode_layer_glu": q4b32_decode_layer_glu,
+    "f16_outproj_residual_4096_ncols8": f16_outproj_residual_4096_ncols8,
+    "q4b32_gate_14336x4096_ncols4": q4b32_gate_14336x4096_ncols4,
 }
 
 

@@ -94,7 +94,8 @@ enum {
     GEMV_OK = 0,
     GEMV_E_NULL = -1,    /* a required pointer (W, x, acc, dst, a view's data) is NULL */
     GEMV_E_DIM = -2,     /* N or K < 1 or too large, K % 32 != 0 for a block
-                            format, or the dst view does not hold N elements */
+                            format, ncols outside 1..GEMV_MAX_NCOLS, or the
+                            dst view does not hold ncols * N elements */
     GEMV_E_FMT = -3,     /* unknown weight format */
     GEMV_E_ACT = -4,     /* unknown epilogue */
     GEMV_E_OPERAND = -5, /* the epilogue's operand is missing, or an operand it
@@ -110,7 +111,8 @@ enum {
 };
 
 #define GEMV_MAX_DIMS 4
-#define GEMV_MAX_DIM_EXTENT (1LL << 31) /* N and K must be below this */
+#define GEMV_MAX_DIM_EXTENT (1LL << 31) /* N, K and ncols * N must be below this */
+#define GEMV_MAX_NCOLS 8
 
 /* A view of f32 device memory: element (i0, .., i_{ndim-1}) lives at
  * data + sum_d i_d * stride[d] (strides in elements).  The library accepts
@@ -169,6 +171,33 @@ int gemv_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t 
 int gemv_glu_validate(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x,
                       int act, const gemv_view *dst);
 
+/* Several destination columns over one W (small-batch or speculative decode).
+ * "feat(cuda): fuse activations and residual add into mmv f/q epilogues",
+ * Summary, states the fused matrix-vector path for one destination column;
+ * this entry widens it to ncols columns, each exactly one gemv_fused column:
+ *     dst[b*N + i] = epilogue((W x_b)_i, operand[b*N + i]),  x_b = x + b*K,
+ * for b < ncols, i < N.  W is streamed from HBM once for all columns.
+ *  x           device pointer to ncols * K f32 values, column b at x + b*K.
+ *  ncols       1..GEMV_MAX_NCOLS (else GEMV_E_DIM).
+ *  mul_operand, add_operand, dst: f32 views of ncols * N elements each, read
+ *              in C order as [ncols][N] (any shape with that flattening, such
+ *              as [ncols, N] or [ncols, 32, 128]); operand rules, the in-place
+ *              case and the overlap rule are those of gemv_fused, with x
+ *              spanning ncols * K floats.
+ * Column b of the result is bit for bit the gemv_fused result for x_b and
+ * operand row b whenever K meets the fast-path conditions (K a multiple of
+ * the 16-byte chunk: 4 f32, 8 f16/bf16 values; always for block formats);
+ * ncols == 1 is gemv_fused itself.  Returns GEMV_OK or a negative status;
+ * asynchronous on hip_stream; allocates nothing. */
+int gemv_fused_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
+                     const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst,
+                     void *hip_stream);
+
+/* The host-side checks of gemv_fused_ncols; no HIP call. */
+int gemv_fused_ncols_validate(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x,
+                              int act, const gemv_view *mul_operand, const gemv_view *add_operand,
+                              const gemv_view *dst);
+
 /* The host-side checks of gemv_fused, with no HIP call and no dereference of
  * any device pointer: returns the status gemv_fused would return before
  * launching.  Safe on a machine with no GPU. */
@@ -200,7 +229,8 @@ int64_t gemv_weight_bytes(int wfmt, int64_t N, int64_t K);
 const char *gemv_strerror(int status);
 
 /* The hipError_t of the last failed launch on the calling thread (0 if
- * none); reset to 0 by every successful gemv_fused / gemv_epilogue call. */
+ * none); reset to 0 by every successful launching call (gemv_fused,
+ * gemv_fused_ncols, gemv_glu, gemv_epilogue). */
 int gemv_last_hip_error(void);
 
 #ifdef __cplusplus

@@ -47,3 +47,29 @@ def check_parity(w, x, act, m=None, r=None, out_shape=None, inplace=False, tag="
     assert np.all(np.isfinite(g)), f"{tag}: non-finite output"
     assert res["max_err"] <= tol, f"{tag}: max_err {res['max_err']:.3e} > {tol} at {res['argmax']} ({res})"
     return g, y, res
+
+
+def run_ncols(w, X, act, M=None, R=None, out_shape=None, inplace=False):
+    B = X.shape[0]
+    shape = tuple(out_shape) if out_shape else (B, w.N)
+    Wd, Xd = dev(w.data), dev(X)
+    Md = dev(M.reshape(shape)) if M is not None else None
+    Rd = dev(R.reshape(shape)) if R is not None else None
+    if inplace:
+        dst = Rd if act == "add" else Md
+    else:
+        dst = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    binding.gemv_fused_ncols(Wd, w.fmt, w.N, w.K, B, Xd, act, mul_operand=Md, add_operand=Rd, dst=dst)
+    torch.cuda.synchronize()
+    return host(dst).reshape(-1).copy()
+
+
+def check_ncols(w, X, act, M=None, R=None, out_shape=None, inplace=False, tag=""):
+    log(f"ncols {tag} fmt={w.fmt} N={w.N} K={w.K} ncols={X.shape[0]} act={act} inplace={inplace}")
+    g = run_ncols(w, X, act, M, R, out_shape, inplace)
+    Y, acc, absacc = oracle.ncols_reference(w.fmt, w.N, w.K, w.data, X, act, M=M, R=R)
+    res = compare(g, Y.reshape(-1), acc.reshape(-1), absacc.reshape(-1), act,
+                  m=None if M is None else M.reshape(-1), r=None if R is None else R.reshape(-1))
+    assert np.all(np.isfinite(g)), tag
+    assert res["max_err"] <= TOLERANCE[w.fmt], f"{tag}: {res}"
+    return g

@@ -203,3 +203,46 @@ def test_glu_validate():
     assert gval(dst=v(U0 + 64, (64,))) == S["GEMV_E_ALIAS"]   # dst on the up matrix
     assert gval(dst=v(W0, (64,))) == S["GEMV_E_ALIAS"]        # dst on the gate matrix
     assert gval(dst=v(X0, (64,))) == S["GEMV_E_ALIAS"]        # dst on x
+
+
+def nval(ncols=4, **kw):
+    args = dict(W=W0, wfmt="f16", N=64, K=64, x=X0, act="none", mul_operand=None, add_operand=None,
+                dst=v(D0, (ncols, 64)))
+    args.update(kw)
+    return b.gemv_fused_ncols_validate(args["W"], args["wfmt"], args["N"], args["K"], ncols, args["x"],
+                                       args["act"], args["mul_operand"], args["add_operand"], args["dst"])
+
+
+def test_ncols_validate():
+    for n in range(1, 9):
+        assert nval(ncols=n) == S["GEMV_OK"]
+    assert nval(ncols=0, dst=v(D0, (1, 64))) == S["GEMV_E_DIM"]
+    assert nval(ncols=9, dst=v(D0, (9, 64))) == S["GEMV_E_DIM"]
+    assert nval(ncols=-1, dst=v(D0, (64,))) == S["GEMV_E_DIM"]
+    # dst must hold ncols * N elements, in any C-contiguous shape
+    assert nval(dst=v(D0, (256,))) == S["GEMV_OK"]
+    assert nval(dst=v(D0, (4, 2, 32))) == S["GEMV_OK"]
+    assert nval(dst=v(D0, (64,))) == S["GEMV_E_DIM"]
+    assert nval(dst=v(D0, (4, 64), (1, 4))) == S["GEMV_E_LAYOUT"]
+    # operands have dst's shape
+    assert nval(act="add", add_operand=v(R0, (4, 64))) == S["GEMV_OK"]
+    assert nval(act="add", add_operand=v(R0, (64,))) == S["GEMV_E_LAYOUT"]
+    assert nval(act="silu_mul", mul_operand=v(M0, (4, 64)), dst=v(M0, (4, 64))) == S["GEMV_OK"]
+    assert nval(act="silu_mul") == S["GEMV_E_OPERAND"]
+    # x spans ncols * K floats: dst right after one column of x still overlaps
+    assert nval(dst=v(X0 + 64 * 4, (4, 64))) == S["GEMV_E_ALIAS"]
+    assert nval(ncols=1, dst=v(X0 + 64 * 4, (1, 64))) == S["GEMV_OK"]
+    # partial overlap with the operand
+    assert nval(act="add", add_operand=v(R0, (4, 64)), dst=v(R0 + 4, (4, 64))) == S["GEMV_E_ALIAS"]
+    assert nval(wfmt="q4b32", K=48) == S["GEMV_E_DIM"]
+    assert nval(W=0) == S["GEMV_E_NULL"]
+    assert nval(act=6) == S["GEMV_E_ACT"]
+
+
+def test_ncols_one_column_matches_gemv_validate():
+    cases = [dict(), dict(act="add", add_operand=v(R0, (64,))), dict(dst=v(X0, (64,))), dict(K=7),
+             dict(wfmt="q8b32", K=40), dict(dst=v(D0, (63,)))]
+    for kw in cases:
+        d = dict(wfmt="f32", dst=v(D0, (64,)))
+        d.update(kw)
+        assert nval(ncols=1, **d) == val(**d), kw

@@ -1,0 +1,177 @@
+"""GPU parity of gemv_fused_ncols (2..8 destination columns over one W)
+against the oracle, and its bit-for-bit agreement with one gemv_fused call per
+column."""
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from oracle.compare import TOLERANCE, compare
+from decode_gemv_elementwise_amd import binding, synth
+from gpu_util import check_ncols, dev, host, log, run_ncols
+
+pytestmark = pytest.mark.gpu
+
+ALL_ACTS = list(synth.ACTS)
+
+
+def _operands(rng, act, B, N):
+    M = rng.normal(size=(B, N)).astype(np.float32) if act in ("silu_mul", "mul") else None
+    R = rng.normal(size=(B, N)).astype(np.float32) if act == "add" else None
+    return M, R
+
+
+SHAPES = [(1, 64), (33, 96), (300, 4096), (1003, 2048), (67, 14336), (17, 4128)]
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("ncols", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_ncols_parity(fmt, ncols, N, K):
+    rng = np.random.default_rng(N * 7 + K + 1000 * ncols)
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(ncols, K)).astype(np.float32)
+    check_ncols(w, X, "none", tag=f"{N}x{K}")
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("act", ALL_ACTS)
+def test_ncols_epilogues(fmt, act):
+    rng = np.random.default_rng(zlib.crc32(f"{fmt}/{act}".encode()))
+    N, K, B = 515, 1024, 3
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(B, K)).astype(np.float32)
+    M, R = _operands(rng, act, B, N)
+    check_ncols(w, X, act, M, R, tag="epilogue")
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N,K", [(5, 7), (64, 1001), (130, 4099)])
+def test_ncols_unaligned_k(fmt, N, K):
+    """Rows that are not whole 16-byte chunks take the element-wise kernel."""
+    rng = np.random.default_rng(N + K)
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(5, K)).astype(np.float32)
+    check_ncols(w, X, "silu", tag="unaligned")
+
+
+def _one_column(w, x, act, m, r):
+    Wd, xd = dev(w.data), dev(x)
+    md = dev(m) if m is not None else None
+    rd = dev(r) if r is not None else None
+    dst = torch.full((w.N,), float("nan"), dtype=torch.float32, device="cuda")
+    binding.gemv_fused(Wd, w.fmt, w.N, w.K, xd, act, mul_operand=md, add_operand=rd, dst=dst)
+    torch.cuda.synchronize()
+    return host(dst).copy()
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("N,K,act", [(300, 4096, "silu_mul"), (67, 14336, "add"), (17, 4128, "sigmoid"),
+                                     (40, 96, "mul")])
+def test_ncols_columns_equal_one_column_calls_bitwise(fmt, N, K, act):
+    rng = np.random.default_rng(N + K + 77)
+    w = synth.random_weights(rng, fmt, N, K)
+    B = 8
+    X = rng.normal(size=(B, K)).astype(np.float32)
+    M, R = _operands(rng, act, B, N)
+    log(f"ncols-vs-one-column fmt={fmt} N={N} K={K} act={act}")
+    g = run_ncols(w, X, act, M, R).reshape(B, N)
+    for b in range(B):
+        one = _one_column(w, X[b], act, None if M is None else M[b], None if R is None else R[b])
+        assert np.array_equal(g[b].view(np.uint32), one.view(np.uint32)), (fmt, b)
+
+
+def test_ncols_odd_k_columns_equal_one_column_calls_bitwise():
+    rng = np.random.default_rng(5)
+    w = synth.random_weights(rng, "f32", 70, 1001)
+    X = rng.normal(size=(4, 1001)).astype(np.float32)
+    g = run_ncols(w, X, "silu").reshape(4, 70)
+    for b in range(4):
+        assert np.array_equal(g[b].view(np.uint32), _one_column(w, X[b], "silu", None, None).view(np.uint32))
+
+
+def test_ncols_one_is_gemv_fused():
+    rng = np.random.default_rng(6)
+    w = synth.random_weights(rng, "q4b32", 257, 4096)
+    x = rng.normal(size=(1, 4096)).astype(np.float32)
+    g = run_ncols(w, x, "silu")
+    assert np.array_equal(g.view(np.uint32), _one_column(w, x[0], "silu", None, None).view(np.uint32))
+
+
+def test_ncols_inplace_and_view():
+    rng = np.random.default_rng(7)
+    w = synth.random_weights(rng, "q8b32", 4096, 6144)
+    B = 4
+    X = rng.normal(size=(B, 6144)).astype(np.float32)
+    R = rng.normal(size=(B, 4096)).astype(np.float32)
+    check_ncols(w, X, "add", R=R, out_shape=(B, 32, 128), tag="view")
+    check_ncols(w, X, "add", R=R, out_shape=(B, 32, 128), inplace=True, tag="view in place")
+    M = rng.normal(size=(B, 4096)).astype(np.float32)
+    check_ncols(w, X, "silu_mul", M=M, inplace=True, tag="silu_mul in place")
+
+
+@pytest.mark.parametrize("fmt,N,K,act", [("q4b32", 14336, 4096, "silu"), ("bf16", 14336, 4096, "silu_mul"),
+                                         ("f16", 4096, 4096, "add"), ("q4b32", 4096, 14336, "add")])
+def test_ncols_full_size(fmt, N, K, act):
+    rng = np.random.default_rng(8)
+    w = synth.random_weights(rng, fmt, N, K)
+    B = 8
+    X = rng.normal(size=(B, K)).astype(np.float32)
+    M, R = _operands(rng, act, B, N)
+    check_ncols(w, X, act, M, R, tag="full size")
+
+
+def test_ncols_zero_and_identity():
+    rng = np.random.default_rng(9)
+    N = K = 256
+    X = rng.normal(size=(6, K)).astype(np.float32)
+    zero = synth.Weights("f16", N, K, np.zeros(N * K, dtype=np.float16).view(np.uint8))
+    g = run_ncols(zero, X, "sigmoid")
+    assert np.all(g == 0.5)
+    eye = synth.Weights("f32", N, K, np.eye(N, K, dtype=np.float32).view(np.uint8).reshape(-1))
+    g = run_ncols(eye, X, "none")
+    assert np.array_equal(g, X.reshape(-1))
+
+
+def test_ncols_rejected_call_writes_nothing():
+    rng = np.random.default_rng(10)
+    w = synth.random_weights(rng, "f16", 64, 64)
+    Wd = dev(w.data)
+    Xd = dev(rng.normal(size=(9, 64)).astype(np.float32))
+    dst = torch.full((9, 64), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.GemvError) as e:
+        binding.gemv_fused_ncols(Wd, "f16", 64, 64, 9, Xd, "none", dst=dst)
+    assert e.value.status == binding.STATUS_CODE["GEMV_E_DIM"]
+    torch.cuda.synchronize()
+    assert torch.all(dst == 7.0)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "q4b32"])
+def test_ncols_x_not_16_byte_aligned(fmt):
+    """x at a 4-byte (not 16-byte) aligned address: the x copies into LDS go a
+    dword at a time; columns still equal the one-column calls bit for bit."""
+    rng = np.random.default_rng(11)
+    N, K, B = 200, 2048, 5
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(B, K)).astype(np.float32)
+    Wd = dev(w.data)
+    buf = torch.zeros(B * K + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = dev(X.reshape(-1))
+    xv = buf[1:]
+    assert xv.data_ptr() % 16 == 4
+    dst = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    log(f"ncols unaligned x fmt={fmt}")
+    binding.gemv_fused_ncols(Wd, fmt, N, K, B, xv, "silu", dst=dst)
+    torch.cuda.synchronize()
+    g = host(dst)
+    Y, acc, absacc = oracle.ncols_reference(fmt, N, K, w.data, X, "silu")
+    res = compare(g.reshape(-1), Y.reshape(-1), acc.reshape(-1), absacc.reshape(-1), "silu")
+    assert res["max_err"] <= TOLERANCE[fmt], res
+    for b in range(B):
+        one = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        binding.gemv_fused(Wd, fmt, N, K, xv[b * K:(b + 1) * K], "silu", dst=one)
+        torch.cuda.synchronize()
+        assert np.array_equal(g[b].view(np.uint32), host(one).view(np.uint32)), b

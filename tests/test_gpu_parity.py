@@ -10,7 +10,7 @@ torch = pytest.importorskip("torch")
 
 import oracle
 from decode_gemv_elementwise_amd import binding, synth
-from gpu_util import check_parity, dev, host, log, run_fused
+from gpu_util import check_ncols, check_parity, dev, host, log, run_fused
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +49,13 @@ def test_workload_calls_full_size(wname):
         if c.w2:
             check_glu(w, wl.weights[c.w2], x, c.act, f"{wname}/{c.name}")
             y = oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act)[0]
+        elif c.ncols > 1:
+            X = np.reshape(x, (c.ncols, w.K))
+            M = None if m is None else np.reshape(m, (c.ncols, w.N))
+            R = None if r is None else np.reshape(r, (c.ncols, w.N))
+            shape = c.out_shape or (c.ncols, w.N)
+            check_ncols(w, X, c.act, M, R, out_shape=shape, inplace=c.inplace, tag=f"{wname}/{c.name}")
+            y = oracle.ncols_reference(w.fmt, w.N, w.K, w.data, X, c.act, M=M, R=R)[0].reshape(-1)
         else:
             g, y, res = check_parity(w, x, c.act, m=m, r=r, out_shape=c.out_shape, inplace=c.inplace,
                                      tag=f"{wname}/{c.name}")
