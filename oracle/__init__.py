@@ -15,7 +15,9 @@ Sources: "feat(cuda): fuse activations and residual add into mmv f/q
 epilogues" (Summary; What changed) for the product and its tails;
 "ggml-cpu: fuse element-wise epilogues (ADD, MUL, SILU) into
 ggml_compute_forward_mul_mat" (What; Correctness) for the multiply tail and
-for the rule that the fused result equals the separate element-wise pass.
+for the rule that the fused result equals the separate element-wise pass;
+"vulkan: fuse the sign multiply into the Hadamard FWHT" (Overview) for the
+signed block Hadamard transform that may precede the product.
 """
 import ctypes
 import os
@@ -59,6 +61,8 @@ def _lib():
         lib.oracle_epilogue.restype = ctypes.c_int
         lib.oracle_glu_epilogue.argtypes = [ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp]
         lib.oracle_glu_epilogue.restype = ctypes.c_int
+        lib.oracle_fwht_signed.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _fp, _fp, _dp, _dp]
+        lib.oracle_fwht_signed.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -201,3 +205,36 @@ def ncols_reference(fmt, N, K, w, X, act, M=None, R=None, rows=None):
         rb = None if R is None else np.asarray(R, dtype=np.float32).reshape(B, N)[b]
         Y[b], acc[b], absacc[b] = reference(fmt, N, K, w, X[b], act, m=mb, r=rb, rows=(b0, e0))
     return Y, acc, absacc
+
+
+def fwht_signed(x, s, n):
+    """Signed Hadamard transform of every row of x ([K] or [rows, K] float32):
+    y = n^-1/2 H_n (x * s) per block of n, the sign of element k being
+    s[k mod len(s)] ("vulkan: fuse the sign multiply into the Hadamard FWHT",
+    Overview; Sylvester order and the orthonormal scale are the readings
+    stated in gemv_oracle.c).  Returns (y, d) in float64 with x's shape, d
+    being n^-1/2 sum |x s| over each output's block."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    s = np.ascontiguousarray(s, dtype=np.float32).reshape(-1)
+    rows = x.reshape(-1, x.shape[-1])
+    K = rows.shape[1]
+    y = np.empty(rows.shape)
+    d = np.empty(rows.shape)
+    for i in range(rows.shape[0]):
+        xi = np.ascontiguousarray(rows[i])
+        rc = _lib().oracle_fwht_signed(n, K, s.size, _ptr(xi, _fp), _ptr(s, _fp), _ptr(y[i], _dp), _ptr(d[i], _dp))
+        if rc != 0:
+            raise ValueError(f"invalid signed FWHT: n={n} K={K} len(s)={s.size}")
+    return y.reshape(x.shape), d.reshape(x.shape)
+
+
+def fwht_gemv_reference(fmt, N, K, w, x, s, n, act, m=None, r=None, rows=None):
+    """The product after the signed transform, as the unfused graph computes
+    it: x' = fwht_signed(x, s, n) rounded to float32 (the transform's output is
+    a float32 tensor), then reference(fmt, N, K, w, x', act, m, r).  Returns
+    (y, acc, absacc) where absacc also carries sum_j |w_ij| d_j, the way the
+    transform's own rounding reaches row i."""
+    xp, d = fwht_signed(x, s, n)
+    y, acc, absacc = reference(fmt, N, K, w, xp.astype(np.float32), act, m=m, r=r, rows=rows)
+    _, absd = gemv(fmt, N, K, w, d.astype(np.float32), rows=rows)
+    return y, acc, absacc + absd

@@ -34,6 +34,13 @@ FLT32_MIN_NORMAL = 2.0 ** -126
 
 TOLERANCE = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "q8b32": 1e-4, "q4b32": 1e-4}
 
+# The signed Hadamard transform in float32: each output is reached through the
+# sign multiply (exact for signs +-1), log2(n) <= 10 add/subtract stages and
+# one scaling, each rounding by at most u = 2^-24 relative to the running
+# magnitude, so |g - y| <= (log2(n) + 2) u d (d = n^-1/2 sum |x s|), under
+# 7.2e-7 for n = 1024.  The gate is err = |g - y| / max(|y|, d) <= 1e-6.
+FWHT_TOLERANCE = 1e-6
+
 
 def _sigmoid(a):
     with np.errstate(over="ignore"):

@@ -10,7 +10,9 @@
  *   1. decode every weight of a row to its exact value (double);
  *   2. acc_i = sum_j w_ij * x_j in double, j ascending, and alongside it
  *      A_i = sum_j |w_ij * x_j| (the magnitude that bounds the rounding error);
- *   3. the epilogue as a SEPARATE pass over the rows, in double with libm exp.
+ *   3. the epilogue as a SEPARATE pass over the rows, in double with libm exp;
+ *   4. (prologue, at the end of the file) the signed Hadamard transform of x,
+ *      each output as its own O(n) sum over Sylvester's matrix.
  *
  * Sources:
  *  - "feat(cuda): fuse activations and residual add into mmv f/q epilogues",
@@ -29,6 +31,8 @@
  *    (planar: codes, then fp16 scales at the next 256-byte boundary; low
  *    nibble = even element) is this project's choice, decoded here from the
  *    written specification, independently of the GPU loaders.
+ *  - "vulkan: fuse the sign multiply into the Hadamard FWHT", Overview: the
+ *    sign multiply and the block Hadamard transform of the activation.
  *
  * Parity pins live in the CPU test-suite: exhaustive fp16/bf16 decode against
  * library conversions, hand-built quantised blocks, exact rational brute force
@@ -239,5 +243,52 @@ int oracle_glu_epilogue(int act, int64_t n, const double *g, const double *u, do
         return ORC_EBAD;
     for (int64_t i = 0; i < n; ++i)
         y[i] = (act == ORC_SILU ? oracle_silu(g[i]) : oracle_sigmoid(g[i])) * u[i];
+    return ORC_OK;
+}
+
+/* ---- signed Hadamard transform, a prologue to the product ----
+ * "vulkan: fuse the sign multiply into the Hadamard FWHT", Overview: the
+ * activation is multiplied element-wise by a sign vector (broadcast over the
+ * sign vector's length), reshaped into blocks, and every block is multiplied
+ * by a Hadamard matrix; the fused dispatch applies the signs while loading
+ * the row, before the transform.  The page fixes neither the matrix's order
+ * nor its scale; the readings taken here: Sylvester's matrix
+ * H[i][j] = (-1)^popcount(i & j) of order n (a power of two), scaled by
+ * 1/sqrt(n) so that the transform is orthonormal, and the sign of element k
+ * of a row is s[k mod ns].
+ *
+ * Plain definition, one O(n) sum per output (no butterflies):
+ *   y[b n + i] = n^-1/2 sum_j H[i][j] x[b n + j] s[(b n + j) mod ns]
+ * in double, j ascending, and alongside it
+ *   d[b n + i] = n^-1/2 sum_j |x[b n + j] s[(b n + j) mod ns]|,
+ * the magnitude that bounds the rounding of any evaluation order.  x, s and
+ * y hold one row of K values. */
+static int popcount_parity(uint64_t v)
+{
+    int p = 0;
+    while (v) {
+        p ^= 1;
+        v &= v - 1;
+    }
+    return p;
+}
+
+int oracle_fwht_signed(int64_t n, int64_t K, int64_t ns, const float *x, const float *s, double *y, double *d)
+{
+    if (n < 1 || (n & (n - 1)) != 0 || K < 1 || K % n != 0 || ns < 1 || K % ns != 0)
+        return ORC_EBAD;
+    const double scale = 1.0 / sqrt((double)n);
+    for (int64_t b = 0; b < K; b += n) {
+        for (int64_t i = 0; i < n; ++i) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                const double v = (double)x[b + j] * (double)s[(b + j) % ns];
+                acc += popcount_parity((uint64_t)(i & j)) ? -v : v;
+                mag += fabs(v);
+            }
+            y[b + i] = acc * scale;
+            d[b + i] = mag * scale;
+        }
+    }
     return ORC_OK;
 }

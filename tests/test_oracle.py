@@ -473,3 +473,106 @@ def test_ncols_pins_catch_transposed_operand():
     wrong = M.reshape(N, B).T.copy()  # the mistaken reading
     Y, *_ = oracle.ncols_reference("f32", N, K, w.data, X, "mul", M=wrong)
     assert any(not np.array_equal(Y[b], dense[:, cols[b]] * M[b].astype(np.float64)) for b in range(B))
+
+
+# ----------------------------------------------------------------- signed Hadamard transform
+
+def test_fwht_small_closed_forms():
+    """n = 1 is the sign multiply; n = 2 is (a + b, a - b) / sqrt 2; the 4-point
+    case worked by hand (signs broadcast with period 2)."""
+    x = np.array([3.0, -5.0, 7.0], np.float32)
+    y, d = oracle.fwht_signed(x, np.array([-1.0], np.float32), 1)
+    assert np.array_equal(y, -x.astype(np.float64)) and np.array_equal(d, np.abs(x).astype(np.float64))
+    y, _ = oracle.fwht_signed(np.array([2.0, 1.0], np.float32), np.array([1.0, 1.0], np.float32), 2)
+    assert np.allclose(y, [3 / math.sqrt(2), 1 / math.sqrt(2)], rtol=1e-15, atol=0)
+    y, d = oracle.fwht_signed(np.array([1, 2, 3, 4], np.float32), np.array([1, -1], np.float32), 4)
+    # (1, -2, 3, -4) against the rows of H_4, over 2
+    assert np.array_equal(y, [-1.0, 5.0, 0.0, -2.0]) and np.array_equal(d, [5.0] * 4)
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 1024])
+def test_fwht_against_scipy_hadamard(n):
+    """Sylvester's matrix from scipy (a library routine) times x * s, over
+    sqrt(n), block by block."""
+    import scipy.linalg
+    rng = np.random.default_rng(n)
+    K = 3 * n
+    x = rng.normal(size=K).astype(np.float32)
+    s = rng.choice([-1.0, 1.0], size=n).astype(np.float32)
+    y, d = oracle.fwht_signed(x, s, n)
+    H = scipy.linalg.hadamard(n).astype(np.float64) / math.sqrt(n)
+    v = (x.astype(np.float64) * np.tile(s, 3)).reshape(3, n)
+    want = (v @ H.T).reshape(-1)
+    assert np.all(np.abs(y - want) <= 4 * n * U * d)
+
+
+def test_fwht_unit_vectors_give_sylvester_columns():
+    """x = e_j gives column j of H_n / sqrt(n): (-1)^popcount(i & j) / sqrt(n).
+    This fixes the natural (Sylvester) order against a sequency (Walsh) order."""
+    n = 16
+    for j in (0, 1, 5, 10, 15):
+        x = np.zeros(n, np.float32)
+        x[j] = 1.0
+        y, _ = oracle.fwht_signed(x, np.ones(1, np.float32), n)
+        want = np.array([(-1.0) ** bin(i & j).count("1") for i in range(n)]) / 4.0
+        assert np.array_equal(y, want), j
+
+
+def test_fwht_parseval_and_involution():
+    """Orthonormal: the sum of squares is kept, and the unsigned transform
+    applied twice gives back x * s."""
+    rng = np.random.default_rng(71)
+    n, K = 256, 1024
+    x = rng.normal(size=K).astype(np.float32)
+    s = rng.choice([-1.0, 1.0], size=K).astype(np.float32)
+    y, d = oracle.fwht_signed(x, s, n)
+    xs = x.astype(np.float64) * s
+    assert abs(np.sum(y * y) - np.sum(xs * xs)) <= 1e-12 * np.sum(xs * xs)
+    y2, _ = oracle.fwht_signed(y.astype(np.float32), np.ones(1, np.float32), n)
+    # y rounded to float32 before the second pass: error of order 2^-24 |y|
+    assert np.max(np.abs(y2 - xs)) <= 1e-6 * np.max(np.abs(xs))
+
+
+def test_fwht_sign_broadcast_period():
+    """The sign of element k is s[k mod len(s)]: a period-3 sign vector over
+    K = 12 (blocks of 4) against the same signs written out at full length."""
+    rng = np.random.default_rng(72)
+    x = rng.normal(size=12).astype(np.float32)
+    s3 = np.array([1.0, -1.0, -1.0], np.float32)
+    y, _ = oracle.fwht_signed(x, s3, 4)
+    y_full, _ = oracle.fwht_signed(x, np.tile(s3, 4), 4)
+    assert np.array_equal(y, y_full)
+    # a plausible mistake -- indexing the signs within the block, k mod n --
+    # gives a different result here
+    wrong, _ = oracle.fwht_signed(x, np.tile(np.tile(s3, 2)[:4], 3), 4)
+    assert not np.array_equal(y, wrong)
+    with pytest.raises(ValueError):
+        oracle.fwht_signed(x, np.ones(5, np.float32), 4)   # 5 does not divide 12
+    with pytest.raises(ValueError):
+        oracle.fwht_signed(x, np.ones(1, np.float32), 3)   # not a power of two
+
+
+def test_fwht_pins_catch_dropped_scale():
+    """Without the 1/sqrt(n) scale the transform is not orthonormal: Parseval
+    fails by a factor n."""
+    rng = np.random.default_rng(73)
+    n = 64
+    x = rng.normal(size=n).astype(np.float32)
+    y, _ = oracle.fwht_signed(x, np.ones(1, np.float32), n)
+    unscaled = y * math.sqrt(n)
+    assert abs(np.sum(unscaled ** 2) / np.sum(x.astype(np.float64) ** 2) - n) < 1e-9
+
+
+def test_fwht_gemv_reference_composition():
+    """The transform feeds the product: with W = the transform's own matrix
+    (f32, n = K = 32, signs +1), W x' = H (H x) / n = x, up to the float32
+    rounding of x'; the error scale covers it."""
+    import scipy.linalg
+    n = K = 32
+    rng = np.random.default_rng(74)
+    x = rng.normal(size=K).astype(np.float32)
+    H = (scipy.linalg.hadamard(n) / math.sqrt(n)).astype(np.float32)
+    y, acc, absacc = oracle.fwht_gemv_reference("f32", n, K, H.view(np.uint8).reshape(-1), x,
+                                                np.ones(1, np.float32), n, "none")
+    assert np.all(np.abs(y - x) <= 1e-6 * absacc)
+    assert np.all(absacc >= np.abs(acc))
