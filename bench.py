@@ -122,6 +122,8 @@ class Step:
                         for c in self.calls}
         self.up_buf = {c.name: torch.zeros((R, wl.weights[c.w].N), dtype=torch.float32, device=dev)
                        for c in self.calls if c.w2}
+        self.xt_buf = {c.name: torch.zeros((R, wl.weights[c.w].K), dtype=torch.float32, device=dev)
+                       for c in self.calls if c.fwht}
         self.prepared = []
         for i in range(R):
             self.prepared.append(self._prepare_set(binding, i, unfused))
@@ -158,6 +160,17 @@ class Step:
                     fns.append(_PreparedEpilogue(binding, "silu_mul", w.N, tmp, up, None, dst))
                 else:
                     fns.append(binding.PreparedGlu(W, W2, w.fmt, w.N, w.K, x, c.act, dst=dst))
+            elif c.fwht:
+                sg = self._vec(c.fwht[0], i)
+                n = c.fwht[1]
+                if unfused:  # the transform into a buffer, then the product reading it
+                    xt = self.xt_buf[c.name][i]
+                    fns.append(binding.PreparedFwht(x, sg, 1, w.K, n, sg.numel(), xt))
+                    fns.append(binding.PreparedCall(W, w.fmt, w.N, w.K, xt, c.act, mul_operand=m, add_operand=r,
+                                                    dst=dst))
+                else:
+                    fns.append(binding.PreparedFusedFwht(W, w.fmt, w.N, w.K, x, sg, n, sg.numel(), c.act,
+                                                         mul_operand=m, add_operand=r, dst=dst))
             elif c.ncols > 1:
                 if unfused and c.act != "none":
                     tmp = self.tmp_buf[c.name][i].view(shape)
@@ -179,7 +192,8 @@ class Step:
         w = self.wl.weights[c.w]
         ops = (1 if c.m else 0) + (1 if c.r else 0)
         w2 = self.wl.weights[c.w2].data.size if c.w2 else 0
-        return w.data.size + w2 + c.ncols * (4 * w.K + 4 * w.N * ops + 4 * w.N)
+        signs = 4 * self.wl.vectors[c.fwht[0]].size if c.fwht else 0
+        return w.data.size + w2 + signs + c.ncols * (4 * w.K + 4 * w.N * ops + 4 * w.N)
 
     def launches_per_step(self):
         return len(self.prepared[0])
@@ -281,6 +295,9 @@ def cpu_baseline(wl, seconds):
             r = wl.vectors[c.r] if c.r else None
             if c.w2:
                 y = oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act)[0]
+            elif c.fwht:
+                y = oracle.fwht_gemv_reference(w.fmt, w.N, w.K, w.data, x, wl.vectors[c.fwht[0]], c.fwht[1], c.act,
+                                               m=m, r=r)[0]
             elif c.ncols > 1:
                 y = oracle.ncols_reference(w.fmt, w.N, w.K, w.data, np.reshape(x, (c.ncols, w.K)), c.act,
                                            M=m, R=r)[0].reshape(-1)
@@ -289,7 +306,8 @@ def cpu_baseline(wl, seconds):
             outputs[c.name] = y.astype(np.float32)
             ops = (1 if c.m else 0) + (1 if c.r else 0)
             w2 = wl.weights[c.w2].data.size if c.w2 else 0
-            nbytes += w.data.size + w2 + c.ncols * (4 * w.K + 4 * w.N * ops + 4 * w.N)
+            signs = 4 * wl.vectors[c.fwht[0]].size if c.fwht else 0
+            nbytes += w.data.size + w2 + signs + c.ncols * (4 * w.K + 4 * w.N * ops + 4 * w.N)
             ncalls += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -347,7 +365,7 @@ def bench_workload(torch, binding, synth, name, args, probe):
             m = "_m_alone"
             vecs[m] = synth.draw_vec(np.random.default_rng(2), dom.ncols * w.N)
         alone = synth.Call(dom.name, dom.w, x, dom.act, m=m, r=dom.r, out_shape=dom.out_shape,
-                           inplace=dom.inplace, w2=dom.w2, ncols=dom.ncols)
+                           inplace=dom.inplace, w2=dom.w2, ncols=dom.ncols, fwht=dom.fwht)
         ws = {dom.w: w}
         if dom.w2:
             ws[dom.w2] = wl.weights[dom.w2]
@@ -361,6 +379,8 @@ def bench_workload(torch, binding, synth, name, args, probe):
     achieved = dom_bytes / dom_sec / 1e9
     if dom.ncols > 1:
         kernel_name = f"gemv_cols_kernel<{dom_w.fmt}, ncols={dom.ncols}> ({dom.name})"
+    elif dom.fwht:
+        kernel_name = f"gemv_fast_kernel<{dom_w.fmt}, signed Hadamard prologue> ({dom.name})"
     else:
         kernel_name = f"gemv_fast_kernel<{dom_w.fmt}{', gated pair' if dom.w2 else ''}> ({dom.name})"
     traffic = read_counters(name)
@@ -380,7 +400,8 @@ def bench_workload(torch, binding, synth, name, args, probe):
         "config": {"workload": name, "calls": [
             {"name": c.name, "wfmt": wl.weights[c.w].fmt, "N": wl.weights[c.w].N, "K": wl.weights[c.w].K,
              "epilogue": (f"{c.act}(gate) * up" if c.w2 else c.act) + (" in place" if c.inplace else "")
-             + (f" view {list(c.out_shape)}" if c.out_shape else ""), **({"ncols": c.ncols} if c.ncols > 1 else {})}
+             + (f" view {list(c.out_shape)}" if c.out_shape else ""), **({"ncols": c.ncols} if c.ncols > 1 else {}),
+             **({"prologue": f"signed FWHT n={c.fwht[1]}"} if c.fwht else {})}
             for c in wl.calls],
             "fused": not args.unfused, "launches_per_step": step.launches_per_step(),
             "launch": args.launch, "rotating_copies": step.copies,

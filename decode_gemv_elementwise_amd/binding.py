@@ -68,6 +68,16 @@ def load(path=None):
     lib.gemv_fused_ncols_validate.argtypes = [_VP, ctypes.c_int, _I64, _I64, _I64, _VP, ctypes.c_int, _VIEWP,
                                               _VIEWP, _VIEWP]
     lib.gemv_fused_ncols_validate.restype = ctypes.c_int
+    lib.gemv_fwht_signed.argtypes = [_VP, _VP, _I64, _I64, _I64, _I64, _VP, _VP]
+    lib.gemv_fwht_signed.restype = ctypes.c_int
+    lib.gemv_fwht_signed_validate.argtypes = [_VP, _VP, _I64, _I64, _I64, _I64, _VP]
+    lib.gemv_fwht_signed_validate.restype = ctypes.c_int
+    lib.gemv_fused_fwht.argtypes = [_VP, ctypes.c_int, _I64, _I64, _VP, _VP, _I64, _I64, ctypes.c_int, _VIEWP,
+                                    _VIEWP, _VIEWP, _VP]
+    lib.gemv_fused_fwht.restype = ctypes.c_int
+    lib.gemv_fused_fwht_validate.argtypes = [_VP, ctypes.c_int, _I64, _I64, _VP, _VP, _I64, _I64, ctypes.c_int,
+                                             _VIEWP, _VIEWP, _VIEWP]
+    lib.gemv_fused_fwht_validate.restype = ctypes.c_int
     lib.gemv_weight_bytes.argtypes = [ctypes.c_int, _I64, _I64]
     lib.gemv_weight_bytes.restype = _I64
     lib.gemv_strerror.argtypes = [ctypes.c_int]
@@ -212,6 +222,32 @@ def gemv_fused_ncols_validate(W, wfmt, N, K, ncols, x, act, mul_operand=None, ad
                                             _as_view(mul_operand), _as_view(add_operand), _as_view(dst))
 
 
+def gemv_fwht_signed(x, signs, nrows, K, n, nsigns, dst, stream=None):
+    """dst = n^-1/2 H_n (x * s) per block of n, for nrows rows of K f32 values."""
+    st = load().gemv_fwht_signed(_addr(x), _addr(signs), nrows, K, n, nsigns, _addr(dst), _stream(stream))
+    if st != 0:
+        _raise(st)
+
+
+def gemv_fwht_signed_validate(x, signs, nrows, K, n, nsigns, dst) -> int:
+    return load().gemv_fwht_signed_validate(_addr(x), _addr(signs), nrows, K, n, nsigns, _addr(dst))
+
+
+def gemv_fused_fwht(W, wfmt, N, K, x, signs, n, nsigns, act, mul_operand=None, add_operand=None, dst=None,
+                    stream=None):
+    """dst = epilogue(W . FWHT_n(x * s)) in one launch."""
+    st = load().gemv_fused_fwht(_addr(W), _fmt(wfmt), N, K, _addr(x), _addr(signs), n, nsigns, _act(act),
+                                _as_view(mul_operand), _as_view(add_operand), _as_view(dst), _stream(stream))
+    if st != 0:
+        _raise(st)
+
+
+def gemv_fused_fwht_validate(W, wfmt, N, K, x, signs, n, nsigns, act, mul_operand=None, add_operand=None,
+                             dst=None) -> int:
+    return load().gemv_fused_fwht_validate(_addr(W), _fmt(wfmt), N, K, _addr(x), _addr(signs), n, nsigns,
+                                           _act(act), _as_view(mul_operand), _as_view(add_operand), _as_view(dst))
+
+
 def gemv_weight_bytes(wfmt, N, K) -> int:
     return int(load().gemv_weight_bytes(_fmt(wfmt), N, K))
 
@@ -265,5 +301,31 @@ class PreparedNcols(PreparedCall):
 
     def __call__(self, stream=None):
         st = self._lib.gemv_fused_ncols(*self._args, *self._ptrs, _stream(stream))
+        if st != 0:
+            _raise(st)
+
+
+class PreparedFusedFwht(PreparedCall):
+    """A gemv_fused_fwht call with its views marshalled once."""
+
+    def __init__(self, W, wfmt, N, K, x, signs, n, nsigns, act, mul_operand=None, add_operand=None, dst=None):
+        super().__init__(W, wfmt, N, K, x, act, mul_operand, add_operand, dst)
+        self._args = (_addr(W), _fmt(wfmt), N, K, _addr(x), _addr(signs), n, nsigns, _act(act))
+
+    def __call__(self, stream=None):
+        st = self._lib.gemv_fused_fwht(*self._args, *self._ptrs, _stream(stream))
+        if st != 0:
+            _raise(st)
+
+
+class PreparedFwht:
+    """A gemv_fwht_signed call with its arguments marshalled once."""
+
+    def __init__(self, x, signs, nrows, K, n, nsigns, dst):
+        self._lib = load()
+        self._args = (_addr(x), _addr(signs), nrows, K, n, nsigns, _addr(dst))
+
+    def __call__(self, stream=None):
+        st = self._lib.gemv_fwht_signed(*self._args, _stream(stream))
         if st != 0:
             _raise(st)

@@ -20,7 +20,7 @@ PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "gemv_kernels.hip"), os.path.join(CSRC, "gemv_cols.hip"),
-           os.path.join(CSRC, "gemv_validate.cpp")]
+           os.path.join(CSRC, "gemv_validate.cpp"), os.path.join(CSRC, "gemv_fwht.hip")]
 PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

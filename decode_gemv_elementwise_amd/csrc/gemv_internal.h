@@ -21,6 +21,12 @@ const char *strerror_of(int status);
 int validate_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
                    const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst);
 
+int validate_fwht(const float *x, const float *signs, int64_t nrows, int64_t K, int64_t n, int64_t nsigns,
+                  const float *dst);
+int validate_fused_fwht(const void *W, int wfmt, int64_t N, int64_t K, const float *x, const float *signs, int64_t n,
+                        int64_t nsigns, int act, const gemv_view *mul_operand, const gemv_view *add_operand,
+                        const gemv_view *dst);
+
 // Records a launch's hipError_t as the calling thread's last HIP error and
 // maps it to GEMV_OK or GEMV_E_HIP.
 int finish_launch(int hip_error);

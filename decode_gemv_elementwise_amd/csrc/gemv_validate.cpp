@@ -201,6 +201,68 @@ int validate_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int6
     return GEMV_OK;
 }
 
+// The signed Hadamard transform's shape rules: n a power of two up to 1024
+// (one wave's tile), dividing K; the sign period dividing K.
+namespace {
+int check_fwht_shape(int64_t K, int64_t n, int64_t nsigns)
+{
+    if (n < 1 || n > 1024 || (n & (n - 1)) != 0 || K % n != 0)
+        return GEMV_E_DIM;
+    if (nsigns < 1 || K % nsigns != 0)
+        return GEMV_E_DIM;
+    return GEMV_OK;
+}
+} // namespace
+
+int validate_fwht(const float *x, const float *signs, int64_t nrows, int64_t K, int64_t n, int64_t nsigns,
+                  const float *dst)
+{
+    if (!x || !signs || !dst)
+        return GEMV_E_NULL;
+    if (nrows < 1 || K < 1 || K >= GEMV_MAX_DIM_EXTENT || nrows * K >= GEMV_MAX_DIM_EXTENT)
+        return GEMV_E_DIM;
+    int st = check_fwht_shape(K, n, nsigns);
+    if (st != GEMV_OK)
+        return st;
+    if (!aligned(x, 4) || !aligned(signs, 4) || !aligned(dst, 4))
+        return GEMV_E_ALIGN;
+    // in place (dst == x) or disjoint; never over the signs
+    Span sd = span_of(dst, nrows * K * 4);
+    if (overlap(sd, span_of(x, nrows * K * 4)) && dst != x)
+        return GEMV_E_ALIAS;
+    if (overlap(sd, span_of(signs, nsigns * 4)))
+        return GEMV_E_ALIAS;
+    return GEMV_OK;
+}
+
+// The product after the transform: the checks of gemv_fused, the transform's
+// shape rules, and the chunked kernel (rows of whole 16-byte chunks, x within
+// the LDS limit), the only one that carries the transform; dst never
+// overlaps the signs.
+int validate_fused_fwht(const void *W, int wfmt, int64_t N, int64_t K, const float *x, const float *signs, int64_t n,
+                        int64_t nsigns, int act, const gemv_view *mul_operand, const gemv_view *add_operand,
+                        const gemv_view *dst)
+{
+    int st = validate(W, wfmt, N, K, x, act, mul_operand, add_operand, dst);
+    if (st != GEMV_OK)
+        return st;
+    if (!signs)
+        return GEMV_E_NULL;
+    st = check_fwht_shape(K, n, nsigns);
+    if (st != GEMV_OK)
+        return st;
+    // weights per 16-byte chunk and LDS floats per chunk of the chunked kernel
+    static const int kE[] = {4, 8, 8, 16, 32}, kXS[] = {4, 12, 12, 20, 36};
+    const int64_t row_bytes = wfmt == GEMV_W_F32 ? K * 4 : (wfmt == GEMV_W_Q8B32 ? K : (wfmt == GEMV_W_Q4B32 ? K / 2 : K * 2));
+    if (row_bytes % 16 != 0 || (K / kE[wfmt]) * kXS[wfmt] * 4 > 160 * 1024)
+        return GEMV_E_DIM;
+    if (!aligned(signs, 4))
+        return GEMV_E_ALIGN;
+    if (overlap(span_of(dst->data, N * 4), span_of(signs, nsigns * 4)))
+        return GEMV_E_ALIAS;
+    return GEMV_OK;
+}
+
 int validate_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul_operand,
                       const gemv_view *add_operand, const gemv_view *dst)
 {
@@ -270,6 +332,19 @@ int gemv_fused_ncols_validate(const void *W, int wfmt, int64_t N, int64_t K, int
                               const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst)
 {
     return gemv::validate_ncols(W, wfmt, N, K, ncols, x, act, mul_operand, add_operand, dst);
+}
+
+int gemv_fwht_signed_validate(const float *x, const float *signs, int64_t nrows, int64_t K, int64_t n, int64_t nsigns,
+                              const float *dst)
+{
+    return gemv::validate_fwht(x, signs, nrows, K, n, nsigns, dst);
+}
+
+int gemv_fused_fwht_validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, const float *signs,
+                             int64_t n, int64_t nsigns, int act, const gemv_view *mul_operand,
+                             const gemv_view *add_operand, const gemv_view *dst)
+{
+    return gemv::validate_fused_fwht(W, wfmt, N, K, x, signs, n, nsigns, act, mul_operand, add_operand, dst);
 }
 
 int gemv_epilogue_validate(int act, int64_t N, const float *acc, const gemv_view *mul_operand,

@@ -22,6 +22,8 @@ Workloads (the decode shapes of a dense 4096-hidden / 14336-FFN layer):
   output), 4096->32 sigmoid.
 * ``q4b32_decode_layer_glu``: the same layer with gate and up as one gated
   pair, silu(W_gate x) * (W_up x) (five calls).
+* ``f16_outproj_fwht_residual_4096``: the f16 residual projection after the
+  signed Hadamard transform of x (blocks of 1024, signs +-1 drawn uniformly).
 * ``f16_outproj_residual_4096_ncols8``, ``q4b32_gate_14336x4096_ncols4``:
   several destination columns over one W (x [ncols, K], operands and dst
   [ncols, N]).
@@ -154,6 +156,7 @@ class Call:
     inplace: bool = False  # dst is the same memory as the add/mul operand
     w2: Optional[str] = None  # up matrix of a gated pair: dst = act(w x) * (w2 x)
     ncols: int = 1  # destination columns: x is [ncols, K], dst and operands [ncols, N]
+    fwht: Optional[Tuple[str, int]] = None  # (signs, n): x goes through the signed Hadamard transform first
 
 
 @dataclass
@@ -237,6 +240,22 @@ def q4b32_decode_layer_glu(seed: int = 0) -> Workload:
                     "the 4-bit decode layer with gate and up as one gated pair")
 
 
+def draw_signs(rng, n: int) -> np.ndarray:
+    return rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=n)
+
+
+def f16_outproj_fwht_residual_4096(seed: int = 0) -> Workload:
+    """The f16 4096x4096 residual projection reading the signed Hadamard
+    transform of x (blocks of 1024, one random sign per element)."""
+    rng = np.random.default_rng(seed)
+    W = draw_float_weights(rng, "f16", 4096, 4096, 1.0 / 4096)
+    x, r = draw_vec(rng, 4096), draw_vec(rng, 4096)
+    sg = draw_signs(rng, 4096)
+    calls = [Call("f16_fwht_outproj_add_inplace", "W", "x", "add", r="r", inplace=True, fwht=("s", 1024))]
+    return Workload("f16_outproj_fwht_residual_4096", {"W": W}, {"x": x, "r": r, "s": sg}, calls,
+                    "dst = W FWHT_1024(x * s) + r in place; W 4096x4096 f16, s +-1")
+
+
 def f16_outproj_residual_4096_ncols8(seed: int = 0) -> Workload:
     """The f16 4096x4096 residual projection over eight destination columns
     (small-batch decode): x [8, 4096], residual [8, 4096], dst = W x_b + r_b in
@@ -267,6 +286,7 @@ WORKLOADS = {
     "q4b32_decode_layer": q4b32_decode_layer,
     "q4b32_decode_layer_glu": q4b32_decode_layer_glu,
     "f16_outproj_residual_4096_ncols8": f16_outproj_residual_4096_ncols8,
+    "f16_outproj_fwht_residual_4096": f16_outproj_fwht_residual_4096,
     "q4b32_gate_14336x4096_ncols4": q4b32_gate_14336x4096_ncols4,
 }
 

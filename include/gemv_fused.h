@@ -198,6 +198,52 @@ int gemv_fused_ncols_validate(const void *W, int wfmt, int64_t N, int64_t K, int
                               int act, const gemv_view *mul_operand, const gemv_view *add_operand,
                               const gemv_view *dst);
 
+/* The signed Hadamard transform ("vulkan: fuse the sign multiply into the
+ * Hadamard FWHT", Overview: the sign multiply applied while the row is
+ * loaded, then the block Hadamard transform, one dispatch):
+ *     dst[r][b n + i] = n^-1/2 sum_j H[i][j] x[r][b n + j] s[(b n + j) mod nsigns]
+ * for every row r < nrows and block b, with H Sylvester's Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i & j)).  The page fixes neither the order nor
+ * the scale of H; this library takes the natural (Sylvester) order and the
+ * orthonormal scale 1/sqrt(n).
+ *  x, dst      device pointers to nrows * K f32 values (rows contiguous); dst
+ *              may be x itself (in place) but may not otherwise overlap x,
+ *              and may not overlap the signs.
+ *  signs       device pointer to nsigns f32 values (typically +-1), applied
+ *              with period nsigns along each row.
+ *  n           block length: a power of two, 1..1024, dividing K.
+ *  nsigns      >= 1, dividing K.
+ * Errors: GEMV_E_NULL, GEMV_E_DIM (shapes; nrows * K must be below
+ * GEMV_MAX_DIM_EXTENT), GEMV_E_ALIGN (4-byte alignment), GEMV_E_ALIAS,
+ * GEMV_E_HIP.  One launch on hip_stream; allocates nothing. */
+int gemv_fwht_signed(const float *x, const float *signs, int64_t nrows, int64_t K, int64_t n, int64_t nsigns,
+                     float *dst, void *hip_stream);
+
+/* The host-side checks of gemv_fwht_signed; no HIP call. */
+int gemv_fwht_signed_validate(const float *x, const float *signs, int64_t nrows, int64_t K, int64_t n,
+                              int64_t nsigns, const float *dst);
+
+/* The product after the signed Hadamard transform, in one launch: each
+ * workgroup transforms x while staging it (the signs applied as x is loaded)
+ * and then streams W as gemv_fused does:
+ *     dst = epilogue(W . FWHT_n(x * s))
+ * Arguments as for gemv_fused, plus signs, n and nsigns as for
+ * gemv_fwht_signed (one row of K values).  The transform uses the same code
+ * as gemv_fwht_signed, so the result is bit for bit gemv_fwht_signed into a
+ * buffer followed by gemv_fused on it.  Carried by the chunked kernel only:
+ * rows must be whole 16-byte chunks (K a multiple of 4 for f32, 8 for
+ * f16/bf16, 32 for the block formats) and x must fit its LDS staging (K up
+ * to 40960 for f32, 27306 for f16/bf16); otherwise GEMV_E_DIM.  dst may not
+ * overlap the signs. */
+int gemv_fused_fwht(const void *W, int wfmt, int64_t N, int64_t K, const float *x, const float *signs, int64_t n,
+                    int64_t nsigns, int act, const gemv_view *mul_operand, const gemv_view *add_operand,
+                    const gemv_view *dst, void *hip_stream);
+
+/* The host-side checks of gemv_fused_fwht; no HIP call. */
+int gemv_fused_fwht_validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, const float *signs,
+                             int64_t n, int64_t nsigns, int act, const gemv_view *mul_operand,
+                             const gemv_view *add_operand, const gemv_view *dst);
+
 /* The host-side checks of gemv_fused, with no HIP call and no dereference of
  * any device pointer: returns the status gemv_fused would return before
  * launching.  Safe on a machine with no GPU. */
@@ -230,7 +276,8 @@ const char *gemv_strerror(int status);
 
 /* The hipError_t of the last failed launch on the calling thread (0 if
  * none); reset to 0 by every successful launching call (gemv_fused,
- * gemv_fused_ncols, gemv_glu, gemv_epilogue). */
+ * gemv_fused_ncols, gemv_glu, gemv_epilogue, gemv_fwht_signed,
+ * gemv_fused_fwht). */
 int gemv_last_hip_error(void);
 
 #ifdef __cplusplus

@@ -246,3 +246,57 @@ def test_ncols_one_column_matches_gemv_validate():
         d = dict(wfmt="f32", dst=v(D0, (64,)))
         d.update(kw)
         assert nval(ncols=1, **d) == val(**d), kw
+
+
+def fval(**kw):
+    args = dict(x=X0, signs=M0, nrows=2, K=4096, n=1024, nsigns=4096, dst=D0)
+    args.update(kw)
+    return b.gemv_fwht_signed_validate(args["x"], args["signs"], args["nrows"], args["K"], args["n"],
+                                       args["nsigns"], args["dst"])
+
+
+def test_fwht_validate():
+    assert fval() == S["GEMV_OK"]
+    for n in (1, 2, 64, 512, 1024):
+        assert fval(n=n) == S["GEMV_OK"]
+    assert fval(n=2048, K=4096) == S["GEMV_E_DIM"]          # beyond one wave's tile
+    assert fval(n=3) == S["GEMV_E_DIM"]                     # not a power of two
+    assert fval(n=0) == S["GEMV_E_DIM"]
+    assert fval(K=1536, n=1024, nsigns=512) == S["GEMV_E_DIM"]   # n does not divide K
+    assert fval(nsigns=3) == S["GEMV_E_DIM"]                # nsigns does not divide K
+    assert fval(nsigns=1) == S["GEMV_OK"]
+    assert fval(nrows=0) == S["GEMV_E_DIM"]
+    assert fval(nrows=1 << 20, K=4096) == S["GEMV_E_DIM"]   # nrows * K too large
+    assert fval(x=0) == S["GEMV_E_NULL"] and fval(signs=0) == S["GEMV_E_NULL"] and fval(dst=0) == S["GEMV_E_NULL"]
+    assert fval(x=X0 + 2) == S["GEMV_E_ALIGN"] and fval(signs=M0 + 1) == S["GEMV_E_ALIGN"]
+    assert fval(dst=X0) == S["GEMV_OK"]                     # in place
+    assert fval(dst=X0 + 4) == S["GEMV_E_ALIAS"]            # shifted overlap
+    assert fval(dst=M0) == S["GEMV_E_ALIAS"]                # over the signs
+    assert fval(x=X0 + 4, dst=X0 + 4, K=7, n=1, nsigns=7) == S["GEMV_OK"]   # any K for n = 1
+
+
+def ffval(**kw):
+    args = dict(W=W0, wfmt="f16", N=64, K=4096, x=X0, signs=M0, n=1024, nsigns=4096, act="add",
+                mul_operand=None, add_operand=v(R0, (64,)), dst=v(D0, (64,)))
+    args.update(kw)
+    return b.gemv_fused_fwht_validate(args["W"], args["wfmt"], args["N"], args["K"], args["x"], args["signs"],
+                                      args["n"], args["nsigns"], args["act"], args["mul_operand"],
+                                      args["add_operand"], args["dst"])
+
+
+def test_fused_fwht_validate():
+    assert ffval() == S["GEMV_OK"]
+    assert ffval(wfmt="q4b32", K=14336, nsigns=1024) == S["GEMV_OK"]
+    assert ffval(signs=0) == S["GEMV_E_NULL"]
+    assert ffval(n=2048) == S["GEMV_E_DIM"]
+    assert ffval(nsigns=3) == S["GEMV_E_DIM"]
+    # only the chunked kernel carries the transform: whole 16-byte chunks, x within LDS
+    assert ffval(wfmt="f16", K=4100, n=4, nsigns=4) == S["GEMV_E_DIM"]
+    assert ffval(wfmt="f32", K=4100, n=4, nsigns=4) == S["GEMV_OK"]
+    assert ffval(wfmt="f16", K=32768, nsigns=1) == S["GEMV_E_DIM"]
+    assert ffval(wfmt="q4b32", K=32768, nsigns=1) == S["GEMV_OK"]
+    assert ffval(dst=v(M0, (64,))) == S["GEMV_E_ALIAS"]      # dst over the signs
+    assert ffval(signs=M0 + 2) == S["GEMV_E_ALIGN"]
+    # the gemv_fused checks come first
+    assert ffval(act="add", add_operand=None) == S["GEMV_E_OPERAND"]
+    assert ffval(dst=v(X0, (64,))) == S["GEMV_E_ALIAS"]

@@ -49,6 +49,12 @@ def test_workload_calls_full_size(wname):
         if c.w2:
             check_glu(w, wl.weights[c.w2], x, c.act, f"{wname}/{c.name}")
             y = oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act)[0]
+        elif c.fwht:
+            from test_gpu_fwht import check_fused_fwht
+            sg = wl.vectors[c.fwht[0]]
+            check_fused_fwht(w, x, sg, c.fwht[1], c.act, m=m, r=r, tag=f"{wname}/{c.name}",
+                             out_shape=c.out_shape, inplace=c.inplace)
+            y = oracle.fwht_gemv_reference(w.fmt, w.N, w.K, w.data, x, sg, c.fwht[1], c.act, m=m, r=r)[0]
         elif c.ncols > 1:
             X = np.reshape(x, (c.ncols, w.K))
             M = None if m is None else np.reshape(m, (c.ncols, w.N))
