@@ -318,6 +318,43 @@ def cpu_baseline(wl, seconds):
             "us_per_call": round(el / ncalls * 1e6, 1)}
 
 
+def cpu_fused_baseline(wl, seconds):
+    """The CPU comparison GEMV (tile-fused epilogue, AVX2 vectors, every host
+    core) on the same workload's full calls, fused and unfused, for about
+    `seconds` of wall time each; None when a call kind has no CPU path."""
+    from decode_gemv_elementwise_amd import cpu_fused
+    if not cpu_fused.available():
+        return None
+    if any(c.w2 or c.ncols > 1 or c.fwht for c in wl.calls):
+        return None
+    threads = len(os.sched_getaffinity(0))
+    out = {}
+    for fused in (True, False):
+        outputs = {}
+        t0 = time.perf_counter()
+        steps = 0
+        while True:
+            for c in wl.calls:
+                w = wl.weights[c.w]
+                x = outputs[c.x[1:]] if c.x.startswith("@") else wl.vectors[c.x]
+                m = (outputs[c.m[1:]] if c.m.startswith("@") else wl.vectors[c.m]) if c.m else None
+                r = wl.vectors[c.r] if c.r else None
+                outputs[c.name] = cpu_fused.gemv(w.fmt, w.N, w.K, w.data, x, c.act, m=m, r=r, threads=threads,
+                                                 fused=fused)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        out["fused" if fused else "unfused"] = el / steps
+    nbytes = sum(wl.weights[c.w].data.size + 4 * wl.weights[c.w].K
+                 + 4 * wl.weights[c.w].N * (1 + (1 if c.m else 0) + (1 if c.r else 0)) for c in wl.calls)
+    return {"value": round(nbytes / out["fused"] / 1e9, 3), "unit": "GB/s", "threads": threads,
+            "kind": "tile-fused vectorised CPU GEMV", "us_per_step": round(out["fused"] * 1e6, 1),
+            "unfused_us_per_step": round(out["unfused"] * 1e6, 1),
+            "sample": f"full steps of {wl.name} for about {seconds:.0f} s each, fused and unfused, "
+                      f"{threads} host threads"}
+
+
 def read_counters(workload):
     """Per-launch HBM traffic (bytes) from the committed rocprofv3 counter
     summary of this workload's dominant kernel, if it was taken on the current
@@ -460,6 +497,8 @@ def main():
         if i == 0 and args.cpu_seconds > 0:
             log("cpu baseline (oracle)")
             res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+            log("cpu comparison (tile-fused GEMV, all host cores)")
+            res["cpu_fused"] = cpu_fused_baseline(wl, args.cpu_seconds / 2)
         print(json.dumps(res), flush=True)
 
 

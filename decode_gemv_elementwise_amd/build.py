@@ -22,6 +22,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = [os.path.join(CSRC, "gemv_kernels.hip"), os.path.join(CSRC, "gemv_cols.hip"),
            os.path.join(CSRC, "gemv_validate.cpp"), os.path.join(CSRC, "gemv_fwht.hip")]
 PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
+CPU_SOURCE = os.path.join(HERE, "cpu", "cpu_fused.c")
+CPU_LIB = os.path.join(HERE, "libcpu_fused.so")
+# the CPU comparison GEMV: AVX2 + FMA + F16C hosts
+CPU_FLAGS = ["-O3", "-std=c11", "-fPIC", "-shared", "-pthread", "-mavx2", "-mfma", "-mf16c", "-ffp-contract=fast",
+             "-Wall"]
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -33,7 +38,7 @@ def _run(cmd, verbose):
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        raise RuntimeError(f"build step failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
 
 
 def _compile(sources, out, verbose, extra_flags=()):
@@ -50,9 +55,18 @@ def _compile(sources, out, verbose, extra_flags=()):
     return out
 
 
+def build_cpu(verbose: bool = False) -> str:
+    tmp = CPU_LIB + ".tmp"
+    _run(["gcc", *CPU_FLAGS, "-I", INCLUDE, "-o", tmp, CPU_SOURCE, "-lm"], verbose)
+    os.replace(tmp, CPU_LIB)
+    return CPU_LIB
+
+
 def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
-    """Builds the GEMV library and the benchmark's measurement library."""
+    """Builds the GEMV library, the benchmark's measurement library and the
+    CPU comparison GEMV."""
     _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    build_cpu(verbose)
     return _compile(SOURCES, out, verbose, extra_flags)
 
 

@@ -1,0 +1,112 @@
+"""The CPU comparison GEMV (tile-fused epilogue, vectorised, threaded)
+against the oracle, and its fused-versus-unfused behaviour: ADD, MUL and NONE
+bit-identical, SIGMOID and SILU within 2 ulp where the vector/remainder split
+moves ("ggml-cpu: fuse element-wise epilogues (ADD, MUL, SILU) into
+ggml_compute_forward_mul_mat", Correctness)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.compare import TOLERANCE, compare
+from decode_gemv_elementwise_amd import cpu_fused, synth
+
+pytestmark = pytest.mark.skipif(not cpu_fused.available(), reason="needs the AVX2/FMA/F16C build of the CPU GEMV")
+
+
+def ulp_distance(a, b):
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    a = np.where(a < 0, -(a & 0x7FFFFFFF), a)
+    b = np.where(b < 0, -(b & 0x7FFFFFFF), b)
+    return np.abs(a - b)
+
+
+def test_vector_exp_within_two_ulp():
+    x = np.concatenate([np.linspace(-87.0, 0.0, 200000), -np.logspace(-30, 1.9, 40000), [0.0] * 8])
+    x = x[: x.size // 8 * 8].astype(np.float32)
+    got = cpu_fused.vexp_nonpos(x)
+    want = np.array([math.exp(v) for v in x.astype(np.float64)], np.float32)
+    assert ulp_distance(got, want).max() <= 2
+
+
+def _operands(rng, act, N):
+    m = rng.normal(size=N).astype(np.float32) if act in ("silu_mul", "mul") else None
+    r = rng.normal(size=N).astype(np.float32) if act == "add" else None
+    return m, r
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("act", list(synth.ACTS))
+def test_cpu_gemv_matches_oracle(fmt, act):
+    rng = np.random.default_rng(len(act) + 7 * synth.FORMATS.index(fmt))
+    N, K = 203, 1024 if fmt.startswith("q") else 1003
+    w = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    m, r = _operands(rng, act, N)
+    y, acc, absacc = oracle.reference(fmt, N, K, w.data, x, act, m=m, r=r)
+    for fused in (True, False):
+        g = cpu_fused.gemv(fmt, N, K, w.data, x, act, m=m, r=r, threads=3, fused=fused)
+        res = compare(g, y, acc, absacc, act, m=m, r=r)
+        assert res["max_err"] <= TOLERANCE[fmt], (fused, res)
+
+
+@pytest.mark.parametrize("act", ["none", "add", "mul"])
+@pytest.mark.parametrize("threads", [1, 3, 8])
+def test_fused_equals_unfused_bitwise_for_add_mul(act, threads):
+    rng = np.random.default_rng(threads)
+    N, K = 1003, 512
+    w = synth.random_weights(rng, "q8b32", N, K)
+    x = synth.draw_vec(rng, K)
+    m, r = _operands(rng, act, N)
+    a = cpu_fused.gemv("q8b32", N, K, w.data, x, act, m=m, r=r, threads=threads, fused=True)
+    b = cpu_fused.gemv("q8b32", N, K, w.data, x, act, m=m, r=r, threads=threads, fused=False)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("act", ["sigmoid", "silu", "silu_mul"])
+def test_fused_vs_unfused_silu_two_ulp_and_aligned_identity(act):
+    rng = np.random.default_rng(11)
+    N, K = 1003, 512
+    w = synth.random_weights(rng, "f16", N, K)
+    x = synth.draw_vec(rng, K)
+    m, _ = _operands(rng, act, N)
+    a = cpu_fused.gemv("f16", N, K, w.data, x, act, m=m, threads=3, fused=True)
+    b = cpu_fused.gemv("f16", N, K, w.data, x, act, m=m, threads=3, fused=False)
+    d = ulp_distance(a, b)
+    assert d.max() <= 2
+    assert d.max() >= 1   # row ranges of 334 split the vector groups differently
+    # one thread and N a multiple of 16: the tiles line up with the vector groups
+    N2 = 1008
+    w2 = synth.random_weights(rng, "f16", N2, K)
+    m2, _ = _operands(rng, act, N2)
+    a = cpu_fused.gemv("f16", N2, K, w2.data, x, act, m=m2, threads=1, fused=True)
+    b = cpu_fused.gemv("f16", N2, K, w2.data, x, act, m=m2, threads=1, fused=False)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_thread_count_does_not_change_the_sums():
+    rng = np.random.default_rng(12)
+    N, K = 777, 4096
+    w = synth.random_weights(rng, "q4b32", N, K)
+    x = synth.draw_vec(rng, K)
+    ref = cpu_fused.gemv("q4b32", N, K, w.data, x, "none", threads=1)
+    for t in (2, 5, 8):
+        assert np.array_equal(ref.view(np.uint32), cpu_fused.gemv("q4b32", N, K, w.data, x, "none", threads=t).view(np.uint32))
+
+
+def test_in_place_add_and_rejections():
+    rng = np.random.default_rng(13)
+    N, K = 64, 256
+    w = synth.random_weights(rng, "bf16", N, K)
+    x = synth.draw_vec(rng, K)
+    r = rng.normal(size=N).astype(np.float32)
+    want = cpu_fused.gemv("bf16", N, K, w.data, x, "add", r=r.copy())
+    rr = r.copy()
+    cpu_fused.gemv("bf16", N, K, w.data, x, "add", r=rr, out=rr)
+    assert np.array_equal(rr, want)
+    with pytest.raises(ValueError):
+        cpu_fused.gemv("q4b32", N, 48, np.zeros(4096, np.uint8), x[:48], "none")
+    with pytest.raises(ValueError):
+        cpu_fused.gemv("f16", N, K, w.data, x, "add")
