@@ -13,10 +13,10 @@
 // Layout of the work, per workgroup of kWaves waves and a tile of kWaves * R
 // rows (wave w owns rows tile*kWaves*R + w*R + [0, R)):
 //  * K is walked in segments of 64 * U chunks.  A segment of x, for all
-//    columns, is staged in LDS (ncols planes of 64 * U * E floats); the next
-//    segment's x is loaded into registers while the current one is used, and
-//    the next segment's W batch (R rows x U chunks per lane) is in flight
-//    while the current batch is consumed.
+//    columns, is copied global -> LDS with direct-to-LDS loads into one of
+//    two buffers (ncols planes of 64 * U * E floats each): the next
+//    segment's copy and W batch (R rows x U chunks per lane) are in flight
+//    while the current segment is consumed.
 //  * Lane l owns chunks l, l + 64, ... of each row, in the same order as the
 //    one-column kernel, and the row sums are reduced with the same wave
 //    reduction: column b of the result is bit for bit the one-column result.
@@ -67,18 +67,6 @@ template <int FMT, int NC> struct ColsCfg {
     static constexpr int kCopies = kBuf4 / kWave;                // 64-slot wave copies per segment
     static constexpr int kDma = (kCopies + kWaves - 1) / kWaves; // copies per wave (the last may be idle)
 };
-
-// Physical float4 slot of float4 f of a plane: the E/4 pieces of chunk
-// c = f / (E/4) are permuted by an XOR with bits of c, so that for any 8 (or
-// 16) consecutive chunks read by consecutive lanes the same piece lands in 8
-// (or 16) distinct 16-byte bank groups.
-template <int FMT> __device__ __forceinline__ int swz(int f)
-{
-    constexpr int P = Fmt<FMT>::E / 4;        // pieces per chunk: 1, 2, 4 or 8
-    constexpr int e = P == 1 ? 0 : (P == 2 ? 1 : (P == 4 ? 2 : 3));
-    const int c = f >> e;
-    return f ^ (((c >> (3 - e)) ^ (c >> (4 - e))) & (P - 1));
-}
 
 // Copies segment seg of x (all columns) from global memory straight into an
 // LDS buffer (global_load_lds): a wave's 16-byte copy fills 64 consecutive

@@ -359,6 +359,18 @@ __device__ __forceinline__ void issue_batch(Batch<FMT, R, U> &b, const unsigned 
     }
 }
 
+// Physical float4 slot of float4 f of an unpadded x plane in LDS: the E/4 pieces of chunk
+// c = f / (E/4) are permuted by an XOR with bits of c, so that for any 8 (or
+// 16) consecutive chunks read by consecutive lanes the same piece lands in 8
+// (or 16) distinct 16-byte bank groups.
+template <int FMT> __device__ __forceinline__ int swz(int f)
+{
+    constexpr int P = Fmt<FMT>::E / 4;        // pieces per chunk: 1, 2, 4 or 8
+    constexpr int e = P == 1 ? 0 : (P == 2 ? 1 : (P == 4 ? 2 : 3));
+    const int c = f >> e;
+    return f ^ (((c >> (3 - e)) ^ (c >> (4 - e))) & (P - 1));
+}
+
 // Workgroup barrier for LDS only: waits for this wave's LDS writes, not for
 // its outstanding global loads.
 __device__ __forceinline__ void lds_barrier()
