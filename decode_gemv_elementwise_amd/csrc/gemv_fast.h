@@ -36,6 +36,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <mutex>
 
@@ -549,17 +550,35 @@ template <int FMT, bool GLU> hipError_t launch_generic(const Call &c, hipStream_
 #ifndef GEMV_MIN_TILES
 #define GEMV_MIN_TILES 512
 #endif
+#ifndef GEMV_ADAPT_WAVES
+#define GEMV_ADAPT_WAVES 1
+#endif
 template <int FMT> constexpr int waves_of() { return Fmt<FMT>::kBlock ? GEMV_WAVES_BLOCK : GEMV_WAVES_FLOAT; }
 constexpr int kLoadsPerLane = GEMV_LOADS_PER_LANE; // R * U target
+
+// Compute units of the current device (queried once per device).
+inline int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 // Rows per wave for a batch of U chunk loads per row: about kLoadsPerLane
 // loads of 16 bytes per lane in flight.  A row longer than one batch (more
 // than 8 chunks per lane) is streamed one row per wave, double-buffered.
 // A gated pair loads two rows (gate and up) per output row, so it takes half
 // as many output rows per wave.
-template <int FMT, int U, bool GLU, bool FWHT = false> hipError_t launch_u(const Call &c, hipStream_t s, bool multi)
+template <int FMT, int kWaves, int U, bool GLU, bool FWHT> hipError_t launch_uw(const Call &c, hipStream_t s, bool multi)
 {
-    constexpr int kWaves = waves_of<FMT>();
     constexpr int R1 = U >= kLoadsPerLane ? 1 : (2 * U > kLoadsPerLane ? 1 : (4 * U > kLoadsPerLane ? 2 : (8 * U > kLoadsPerLane ? 4 : 8)));
     constexpr int R0 = GLU ? (R1 > 1 ? R1 / 2 : 1) : R1;
     // Every workgroup transforms all of x itself, so with the Hadamard
@@ -575,6 +594,34 @@ template <int FMT, int U, bool GLU, bool FWHT = false> hipError_t launch_u(const
     if (!FWHT && R > 1 && tiles < GEMV_MIN_TILES)
         return launch_fast<FMT, kWaves, 1, U, false, GLU, FWHT>(c, s);
     return launch_fast<FMT, kWaves, R, U, false, GLU, FWHT>(c, s);
+}
+
+// Waves per workgroup for the float formats' one-column calls, from the
+// shape (measured on MI355X across N = 32..28672, K = 4096..14336): long rows
+// stream best with 16 waves from three batches per row up (one workgroup per
+// CU by LDS) and with 8 at two batches, as long as every CU still gets a
+// workgroup; one batch per row
+// and rows that fill exactly one 16-wave workgroup per CU take 16 waves (one
+// copy of x staged per CU); everything else keeps the 4-wave tiles, whose
+// finer grain balances the many-workgroup shapes.  The choice depends only on
+// (format, N, K), so the reduction order of a row (one wave, lanes over its
+// chunks) is the same whatever it picks.
+template <int FMT, int U, bool GLU, bool FWHT = false> hipError_t launch_u(const Call &c, hipStream_t s, bool multi)
+{
+    if constexpr (!Fmt<FMT>::kBlock && !GLU && !FWHT && GEMV_ADAPT_WAVES) {
+        const int64_t cus = device_cus();
+        if (multi && U >= 5) {
+            const int cpl = (c.K / Fmt<FMT>::E + kWave - 1) / kWave;
+            const int nbatch = (cpl + 7) / 8;
+            if (nbatch >= 3 && (c.N + 15) / 16 >= cus)
+                return launch_uw<FMT, 16, U, GLU, FWHT>(c, s, multi);
+            if ((c.N + 7) / 8 >= cus)
+                return launch_uw<FMT, 8, U, GLU, FWHT>(c, s, multi);
+        } else if (!multi && U >= kLoadsPerLane && (c.N + 15) / 16 == cus) {
+            return launch_uw<FMT, 16, U, GLU, FWHT>(c, s, multi);
+        }
+    }
+    return launch_uw<FMT, waves_of<FMT>(), U, GLU, FWHT>(c, s, multi);
 }
 
 // The path depends only on (format, N, K), never on the epilogue, so a fused

@@ -416,3 +416,20 @@ def test_glu_rejected_writes_nothing():
     assert e.value.status == binding.STATUS_CODE["GEMV_E_ACT"]
     torch.cuda.synchronize()
     assert torch.all(dst == 3.0)
+
+
+# ------------------------------------------------------------------ shape-chosen wave counts
+
+@pytest.mark.parametrize("fmt,N,K", [("f16", 4096, 14336), ("bf16", 4096, 6144), ("f32", 4096, 4096),
+                                     ("f16", 4096, 4096), ("bf16", 2048, 14336), ("f16", 4095, 4096)])
+def test_wave_count_paths(fmt, N, K):
+    """Shapes that take the 16- and 8-wave workgroups (long rows; rows that
+    fill one 16-wave workgroup per CU) against the oracle, and fused ==
+    unfused bit for bit on them."""
+    rng = np.random.default_rng(N + K)
+    w = synth.random_weights(rng, fmt, N, K)
+    x = synth.draw_vec(rng, K)
+    r = rng.normal(size=N).astype(np.float32)
+    check_parity(w, x, "add", r=r, tag=f"waves {N}x{K}")
+    f, u = _fused_and_unfused(w, x, "silu_mul", rng.normal(size=N).astype(np.float32), None)
+    assert np.array_equal(f.view(np.uint32), u.view(np.uint32))
