@@ -11,7 +11,9 @@
 // from the HBM roof towards the VALU roof.
 //
 // Layout of the work, per workgroup of kWaves waves and a tile of kWaves * R
-// rows (wave w owns rows tile*kWaves*R + w*R + [0, R)):
+// rows (wave w owns rows tile*kWaves*R + w*R + [0, R)); where a row fits one
+// segment and x of every column fits LDS, a "one-shot" variant stages x once
+// and issues every chunk of the wave's rows up front (see dispatch_cols):
 //  * K is walked in segments of 64 * U chunks.  A segment of x, for all
 //    columns, is copied global -> LDS with direct-to-LDS loads into one of
 //    two buffers (ncols planes of 64 * U * E floats each): the next
@@ -50,17 +52,25 @@ namespace {
 #ifndef GEMV_COLS_SERIAL
 #define GEMV_COLS_SERIAL 1
 #endif
+#ifndef GEMV_COLS_ONESHOT
+#define GEMV_COLS_ONESHOT 1
+#endif
 
-template <int FMT, int NC> struct ColsCfg {
+// UO == 0: segments of GEMV_COLS_X_BUDGET / (NC * E) chunks per lane.
+// UO > 0: a whole row in one segment of UO chunks per lane ("one-shot": x of
+// every column staged once, every W chunk of the wave's rows issued at once),
+// used when that fits LDS; 8 waves of 2 rows (16 rows per workgroup) keep
+// 2 * UO loads per lane in flight.
+template <int FMT, int NC, int UO = 0> struct ColsCfg {
     static constexpr int E = Fmt<FMT>::E;
-    static constexpr int kWaves = GEMV_COLS_WAVES;
+    static constexpr int kWaves = UO > 0 ? 8 : GEMV_COLS_WAVES;
     // chunks per lane per segment: GEMV_COLS_X_BUDGET / (NC * E), 1..8 (a
     // short segment keeps the LDS per workgroup small and occupancy up)
     static constexpr int kU0 = GEMV_COLS_X_BUDGET / (NC * E);
-    static constexpr int U = kU0 < 1 ? 1 : (kU0 > 8 ? 8 : kU0);
+    static constexpr int U = UO > 0 ? UO : (kU0 < 1 ? 1 : (kU0 > 8 ? 8 : kU0));
     // rows per wave: about GEMV_COLS_LOADS chunk loads per lane per batch, 1..4
     static constexpr int kR0 = GEMV_COLS_LOADS / U;
-    static constexpr int R = kR0 > 4 ? 4 : (kR0 < 1 ? 1 : kR0);
+    static constexpr int R = UO > 0 ? 2 : (kR0 > 4 ? 4 : (kR0 < 1 ? 1 : kR0));
     static constexpr int SEG = 64 * U * E;     // x floats per column per segment
     static constexpr int kPlane4 = SEG / 4;    // float4 slots per plane (a multiple of 64)
     static constexpr int kBuf4 = NC * kPlane4; // float4 slots per segment buffer
@@ -75,11 +85,11 @@ template <int FMT, int NC> struct ColsCfg {
 // 16-byte aligned the same slots are filled by 4-byte copies, 16 slots per
 // instruction.  Elements past K fetch a clamped, valid address; those slots
 // belong to chunks past the end of the row and are never used.
-template <int FMT, int NC>
+template <int FMT, int NC, int UO>
 __device__ __forceinline__ void dma_x_segment(f32x4 *buf, const float *x, int K, int seg, int wave, int lane,
                                               bool aligned16)
 {
-    using C = ColsCfg<FMT, NC>;
+    using C = ColsCfg<FMT, NC, UO>;
     const int k4 = K / 4; // K is a multiple of 4 on this path
     if (aligned16) {
 #pragma unroll
@@ -113,13 +123,13 @@ __device__ __forceinline__ void dma_x_segment(f32x4 *buf, const float *x, int K,
     }
 }
 
-template <int FMT, int NC, int R, int U>
+template <int FMT, int NC, int UO, int R, int U>
 __device__ __forceinline__ void consume_cols(const Batch<FMT, R, U> &b, const f32x4 *xs, float (&acc)[R][NC],
                                              int lane, int chunk0, int nchunks)
 {
     using F = Fmt<FMT>;
     constexpr int P = F::E / 4;
-    constexpr int kPlane4 = ColsCfg<FMT, NC>::kPlane4;
+    constexpr int kPlane4 = ColsCfg<FMT, NC, UO>::kPlane4;
     const f32x4 *xs4 = xs;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -158,13 +168,13 @@ __device__ __forceinline__ void consume_cols(const Batch<FMT, R, U> &b, const f3
     }
 }
 
-template <int FMT, int NC>
-__global__ __launch_bounds__((ColsCfg<FMT, NC>::kWaves * kWave)) void gemv_cols_kernel(
+template <int FMT, int NC, int UO>
+__global__ __launch_bounds__((ColsCfg<FMT, NC, UO>::kWaves * kWave)) void gemv_cols_kernel(
     const unsigned char *__restrict__ W, const float *__restrict__ x, int N, int K, int act, const float *mop,
     const float *rop, float *dst)
 {
     using F = Fmt<FMT>;
-    using C = ColsCfg<FMT, NC>;
+    using C = ColsCfg<FMT, NC, UO>;
     constexpr int R = C::R, U = C::U, SEGC = kWave * C::U;
     // two segment buffers (x of segment s+1 lands in one while segment s is
     // read from the other); a row of one segment gets only the first
@@ -191,7 +201,7 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC>::kWaves * kWave)) void gemv_cols_
 
     // 2. x of the first segment, straight into LDS
     const bool x16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-    dma_x_segment<FMT, NC>(xa, x, K, 0, wave, lane, x16);
+    dma_x_segment<FMT, NC, UO>(xa, x, K, 0, wave, lane, x16);
 
     // 3. W, first batch
     const unsigned char *wrow[R];
@@ -218,23 +228,29 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC>::kWaves * kWave)) void gemv_cols_
     //    waits for all of them; the barrier then makes every wave's copy
     //    visible and guarantees that all waves are done with the other buffer,
     //    which the next segment's copy overwrites.
+    if constexpr (UO > 0) {
+        // the whole row is one segment: one wait, one barrier, one batch
+        __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0); expcnt, lgkmcnt not waited for
+        __builtin_amdgcn_s_barrier();
+        consume_cols<FMT, NC, UO, R, U>(b0, xa, acc, lane, 0, nchunks);
+    } else
     for (int s = 0;;) {
         __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0); expcnt, lgkmcnt not waited for
         __builtin_amdgcn_s_barrier();
         if (s + 1 < nseg) {
-            dma_x_segment<FMT, NC>(xb, x, K, s + 1, wave, lane, x16);
+            dma_x_segment<FMT, NC, UO>(xb, x, K, s + 1, wave, lane, x16);
             issue_batch<FMT, R, U>(b1, wrow, srow, lane, (s + 1) * U, nchunks);
         }
-        consume_cols<FMT, NC, R, U>(b0, xa, acc, lane, s * SEGC, nchunks);
+        consume_cols<FMT, NC, UO, R, U>(b0, xa, acc, lane, s * SEGC, nchunks);
         if (++s == nseg)
             break;
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __builtin_amdgcn_s_barrier();
         if (s + 1 < nseg) {
-            dma_x_segment<FMT, NC>(xa, x, K, s + 1, wave, lane, x16);
+            dma_x_segment<FMT, NC, UO>(xa, x, K, s + 1, wave, lane, x16);
             issue_batch<FMT, R, U>(b0, wrow, srow, lane, (s + 1) * U, nchunks);
         }
-        consume_cols<FMT, NC, R, U>(b1, xb, acc, lane, s * SEGC, nchunks);
+        consume_cols<FMT, NC, UO, R, U>(b1, xb, acc, lane, s * SEGC, nchunks);
         if (++s == nseg)
             break;
     }
@@ -322,10 +338,10 @@ struct ColsCall {
     float *dst;
 };
 
-template <int FMT, int NC> hipError_t launch_cols(const ColsCall &c, hipStream_t s)
+template <int FMT, int NC, int UO> hipError_t launch_cols(const ColsCall &c, hipStream_t s)
 {
-    using C = ColsCfg<FMT, NC>;
-    const void *fn = reinterpret_cast<const void *>(&gemv_cols_kernel<FMT, NC>);
+    using C = ColsCfg<FMT, NC, UO>;
+    const void *fn = reinterpret_cast<const void *>(&gemv_cols_kernel<FMT, NC, UO>);
     const int nchunks = c.K / C::E;
     const int nseg = (nchunks + kWave * C::U - 1) / (kWave * C::U);
     const size_t lds = (size_t)(nseg > 1 ? 2 : 1) * C::kBuf4 * 16;
@@ -366,11 +382,30 @@ template <int FMT, int NC> hipError_t launch_cols_generic(const ColsCall &c, hip
 // kernel (rows of whole 16-byte chunks, x of one column fits the one-column
 // kernel's padded LDS staging), so that every column reduces in the same
 // order as the one-column call.
+// One segment per row (UO chunks per lane) wherever the row fits it and x
+// of every column fits LDS: f16/bf16/f32 up to 8 chunks per lane, the 8-bit
+// format up to 4 and the 4-bit format up to 2 (K <= 4096 for the 16-bit and
+// block formats, 2048 for f32).
+template <int FMT> constexpr int oneshot_u() { return Fmt<FMT>::E <= 8 ? 8 : (Fmt<FMT>::E == 16 ? 4 : 2); }
+
 template <int FMT, int NC> hipError_t dispatch_cols(const ColsCall &c, hipStream_t s)
 {
     const int64_t lds1 = (int64_t)(c.K / Fmt<FMT>::E) * Fmt<FMT>::XS * 4;
     const bool fast = (row_bytes<FMT>(c.K) % 16 == 0) && lds1 <= kMaxLds;
-    return fast ? launch_cols<FMT, NC>(c, s) : launch_cols_generic<FMT, NC>(c, s);
+    if (!fast)
+        return launch_cols_generic<FMT, NC>(c, s);
+    constexpr int UO = oneshot_u<FMT>();
+    const int cpl = (c.K / Fmt<FMT>::E + kWave - 1) / kWave;
+    if constexpr (NC * kWave * UO * Fmt<FMT>::E * 4 <= kMaxLds) {
+        // measured: the block formats gain wherever it fits; the float
+        // formats from 3 columns, while every CU gets a 16-row workgroup and
+        // x of all columns stays within 64 KiB (two workgroups per CU)
+        const int64_t lds = (int64_t)NC * kWave * cpl * Fmt<FMT>::E * 4;
+        const bool take = Fmt<FMT>::kBlock || (NC >= 3 && (c.N + 15) / 16 >= device_cus() && lds <= 64 * 1024);
+        if (GEMV_COLS_ONESHOT && cpl <= UO && take)
+            return launch_cols<FMT, NC, UO>(c, s);
+    }
+    return launch_cols<FMT, NC, 0>(c, s);
 }
 
 template <int NC> hipError_t dispatch_cols_fmt(int wfmt, const ColsCall &c, hipStream_t s)

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "gemv_fused.h"
@@ -369,6 +370,22 @@ template <int FMT> __device__ __forceinline__ int swz(int f)
     constexpr int e = P == 1 ? 0 : (P == 2 ? 1 : (P == 4 ? 2 : 3));
     const int c = f >> e;
     return f ^ (((c >> (3 - e)) ^ (c >> (4 - e))) & (P - 1));
+}
+
+// Compute units of the current device (queried once per device).
+inline int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // Workgroup barrier for LDS only: waits for this wave's LDS writes, not for

@@ -556,22 +556,6 @@ template <int FMT, bool GLU> hipError_t launch_generic(const Call &c, hipStream_
 template <int FMT> constexpr int waves_of() { return Fmt<FMT>::kBlock ? GEMV_WAVES_BLOCK : GEMV_WAVES_FLOAT; }
 constexpr int kLoadsPerLane = GEMV_LOADS_PER_LANE; // R * U target
 
-// Compute units of the current device (queried once per device).
-inline int device_cus()
-{
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // Rows per wave for a batch of U chunk loads per row: about kLoadsPerLane
 // loads of 16 bytes per lane in flight.  A row longer than one batch (more
 // than 8 chunks per lane) is streamed one row per wave, double-buffered.
