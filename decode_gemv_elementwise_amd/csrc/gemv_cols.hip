@@ -213,7 +213,8 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO>::kWaves * kWave)) void gemv_c
         srow[r] = F::kBlock ? scales + (int64_t)row * sbytes : nullptr;
     }
     Batch<FMT, R, U> b0, b1;
-    issue_batch<FMT, R, U>(b0, wrow, srow, lane, 0, nchunks);
+    if constexpr (UO == 0) // one-shot: W follows the wait for x (below)
+        issue_batch<FMT, R, U>(b0, wrow, srow, lane, 0, nchunks);
 
     float acc[R][NC];
 #pragma unroll
@@ -229,9 +230,12 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO>::kWaves * kWave)) void gemv_c
     //    visible and guarantees that all waves are done with the other buffer,
     //    which the next segment's copy overwrites.
     if constexpr (UO > 0) {
-        // the whole row is one segment: one wait, one barrier, one batch
+        // the whole row is one segment: wait for the x copy, barrier, then
+        // issue every W chunk, so that the FMAs wait for each chunk as it
+        // lands (the copy's wait would otherwise have waited for all of W)
         __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0); expcnt, lgkmcnt not waited for
         __builtin_amdgcn_s_barrier();
+        issue_batch<FMT, R, U>(b0, wrow, srow, lane, 0, nchunks);
         consume_cols<FMT, NC, UO, R, U>(b0, xa, acc, lane, 0, nchunks);
     } else
     for (int s = 0;;) {
