@@ -403,9 +403,12 @@ template <int FMT, int NC> hipError_t dispatch_cols(const ColsCall &c, hipStream
     if constexpr (NC * kWave * UO * Fmt<FMT>::E * 4 <= kMaxLds) {
         // measured: the block formats gain wherever it fits; the float
         // formats from 3 columns, while every CU gets a 16-row workgroup and
-        // x of all columns stays within 64 KiB (two workgroups per CU)
+        // either x of all columns stays within 64 KiB (two workgroups per CU)
+        // or the workgroups are one round (one per CU)
         const int64_t lds = (int64_t)NC * kWave * cpl * Fmt<FMT>::E * 4;
-        const bool take = Fmt<FMT>::kBlock || (NC >= 3 && (c.N + 15) / 16 >= device_cus() && lds <= 64 * 1024);
+        const int64_t wgs = (c.N + 15) / 16, cus = device_cus();
+        const bool take = Fmt<FMT>::kBlock ||
+                          (NC >= 3 && wgs >= cus && (lds <= 64 * 1024 || wgs <= cus));
         if (GEMV_COLS_ONESHOT && cpl <= UO && take)
             return launch_cols<FMT, NC, UO>(c, s);
     }
