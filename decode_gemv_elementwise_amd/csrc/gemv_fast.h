@@ -592,14 +592,16 @@ template <int FMT, int kWaves, int U, bool GLU, bool FWHT> hipError_t launch_uw(
 // chunks) is the same whatever it picks.
 template <int FMT, int U, bool GLU, bool FWHT = false> hipError_t launch_u(const Call &c, hipStream_t s, bool multi)
 {
-    if constexpr (!Fmt<FMT>::kBlock && !GLU && !FWHT && GEMV_ADAPT_WAVES) {
+    if constexpr (!Fmt<FMT>::kBlock && !GLU && GEMV_ADAPT_WAVES) {
         const int64_t cus = device_cus();
         if (multi && U >= 5) {
             const int cpl = (c.K / Fmt<FMT>::E + kWave - 1) / kWave;
             const int nbatch = (cpl + 7) / 8;
-            if (nbatch >= 3 && (c.N + 15) / 16 >= cus)
+            // with the prologue a long-row wave takes 2 rows: 8 waves keep the
+            // 16-row workgroups that spread the transform
+            if (!FWHT && nbatch >= 3 && (c.N + 15) / 16 >= cus)
                 return launch_uw<FMT, 16, U, GLU, FWHT>(c, s, multi);
-            if ((c.N + 7) / 8 >= cus)
+            if ((c.N + (FWHT ? 15 : 7)) / (FWHT ? 16 : 8) >= cus)
                 return launch_uw<FMT, 8, U, GLU, FWHT>(c, s, multi);
         } else if (!multi && U >= kLoadsPerLane && (c.N + 15) / 16 == cus) {
             return launch_uw<FMT, 16, U, GLU, FWHT>(c, s, multi);
