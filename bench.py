@@ -33,10 +33,11 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 ROTATE_MIN_BYTES = 512 << 20
 DEFAULT_WORKLOAD = "f16_outproj_residual_4096"
-# the device code of the kernels (entry points and host checks excluded): a
-# counter summary stays valid while these files are unchanged
+# the device code of the one-column kernel (the kernel the counter summaries
+# cover; entry points and host checks excluded): a summary stays valid while
+# these files are unchanged
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_gemv_elementwise_amd", "csrc", f)
-                  for f in ("gemv_device.h", "gemv_fast.h", "gemv_cols.hip")]
+                  for f in ("gemv_device.h", "gemv_fast.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
