@@ -31,6 +31,8 @@ PEAK_HBM_GBPS = 8000.0
 # f32 FMA throughput of the vector ALUs without packed FP32 (the kernels are
 # built with packed FP32 off): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
 PEAK_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# dense f16 matrix-core peak (the matrix-core column kernel runs f16 MFMAs)
+PEAK_MFMA_F16_TFLOPS = 2500.0
 ROTATE_MIN_BYTES = 512 << 20
 DEFAULT_WORKLOAD = "f16_outproj_residual_4096"
 # the device code of the one-column kernel (the kernel the counter summaries
@@ -417,7 +419,10 @@ def bench_workload(torch, binding, synth, name, args, probe):
     dom_w = wl.weights[dom.w]
     dom_flops = 2 * dom_w.N * dom_w.K * dom.ncols * (2 if dom.w2 else 1)
     achieved = dom_bytes / dom_sec / 1e9
-    if dom.ncols > 1:
+    cols_kernel = binding.gemv_ncols_kernel(dom_w.fmt, dom_w.N, dom_w.K, dom.ncols) if dom.ncols > 1 else None
+    if cols_kernel == "columns_matrix":
+        kernel_name = f"gemv_cols_mfma_kernel<{dom_w.fmt}, ncols={dom.ncols}> ({dom.name})"
+    elif dom.ncols > 1:
         kernel_name = f"gemv_cols_kernel<{dom_w.fmt}, ncols={dom.ncols}> ({dom.name})"
     elif dom.fwht:
         kernel_name = f"gemv_fast_kernel<{dom_w.fmt}, signed Hadamard prologue> ({dom.name})"
@@ -455,9 +460,12 @@ def bench_workload(torch, binding, synth, name, args, probe):
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "us_per_launch": round(dom_sec * 1e6, 3)},
     }
-    # one FMA per weight and destination column: where that work at the VALU
-    # peak takes longer than the bytes at the HBM peak, the ALU is the roof
-    if dom_flops / (PEAK_VALU_TFLOPS * 1e12) > dom_bytes / (PEAK_HBM_GBPS * 1e9):
+    # one FMA per weight and destination column: where that work at the peak
+    # of the units that run it (the matrix cores for the matrix-core column
+    # kernel, else the vector ALUs) takes longer than the bytes at the HBM
+    # peak, the ALU is the roof
+    peak_flops = PEAK_MFMA_F16_TFLOPS if cols_kernel == "columns_matrix" else PEAK_VALU_TFLOPS
+    if dom_flops / (peak_flops * 1e12) > dom_bytes / (PEAK_HBM_GBPS * 1e9):
         tflops = dom_flops / dom_sec / 1e12
         res["roofline"].update({"bound": "alu", "achieved": round(tflops, 3), "peak": round(PEAK_VALU_TFLOPS, 1),
                                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_VALU_TFLOPS, 4),

@@ -68,6 +68,8 @@ def load(path=None):
     lib.gemv_fused_ncols_validate.argtypes = [_VP, ctypes.c_int, _I64, _I64, _I64, _VP, ctypes.c_int, _VIEWP,
                                               _VIEWP, _VIEWP]
     lib.gemv_fused_ncols_validate.restype = ctypes.c_int
+    lib.gemv_ncols_kernel.argtypes = [ctypes.c_int, _I64, _I64, _I64]
+    lib.gemv_ncols_kernel.restype = ctypes.c_int
     lib.gemv_fwht_signed.argtypes = [_VP, _VP, _I64, _I64, _I64, _I64, _VP, _VP]
     lib.gemv_fwht_signed.restype = ctypes.c_int
     lib.gemv_fwht_signed_validate.argtypes = [_VP, _VP, _I64, _I64, _I64, _I64, _VP]
@@ -220,6 +222,19 @@ def gemv_fused_ncols(W, wfmt, N, K, ncols, x, act, mul_operand=None, add_operand
 def gemv_fused_ncols_validate(W, wfmt, N, K, ncols, x, act, mul_operand=None, add_operand=None, dst=None) -> int:
     return load().gemv_fused_ncols_validate(_addr(W), _fmt(wfmt), N, K, ncols, _addr(x), _act(act),
                                             _as_view(mul_operand), _as_view(add_operand), _as_view(dst))
+
+
+NCOLS_KERNELS = {1: "one_column", 2: "columns", 3: "columns_generic", 4: "columns_matrix"}
+
+
+def gemv_ncols_kernel(wfmt, N, K, ncols) -> str:
+    """Name of the kernel gemv_fused_ncols takes for this format and shape on
+    the current device ('one_column', 'columns', 'columns_generic',
+    'columns_matrix'); GemvError for arguments it would reject."""
+    st = load().gemv_ncols_kernel(_fmt(wfmt), N, K, ncols)
+    if st < 0:
+        _raise(st)
+    return NCOLS_KERNELS[st]
 
 
 def gemv_fwht_signed(x, signs, nrows, K, n, nsigns, dst, stream=None):

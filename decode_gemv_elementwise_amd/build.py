@@ -20,7 +20,8 @@ PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "gemv_kernels.hip"), os.path.join(CSRC, "gemv_cols.hip"),
-           os.path.join(CSRC, "gemv_validate.cpp"), os.path.join(CSRC, "gemv_fwht.hip")]
+           os.path.join(CSRC, "gemv_validate.cpp"), os.path.join(CSRC, "gemv_fwht.hip"),
+           os.path.join(CSRC, "gemv_mfma.hip")]
 PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
 CPU_SOURCE = os.path.join(HERE, "cpu", "cpu_fused.c")
 CPU_LIB = os.path.join(HERE, "libcpu_fused.so")

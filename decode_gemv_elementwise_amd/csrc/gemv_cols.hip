@@ -55,6 +55,11 @@ namespace {
 #ifndef GEMV_COLS_ONESHOT
 #define GEMV_COLS_ONESHOT 1
 #endif
+// f16 and the block formats take the matrix-core kernel (gemv_mfma.hip)
+// where the shape fits it
+#ifndef GEMV_COLS_MFMA
+#define GEMV_COLS_MFMA 1
+#endif
 
 // UO == 0: segments of GEMV_COLS_X_BUDGET / (NC * E) chunks per lane.
 // UO > 0: a whole row in one segment of UO chunks per lane ("one-shot": x of
@@ -334,13 +339,7 @@ __global__ __launch_bounds__(256) void gemv_cols_generic_kernel(const unsigned c
 
 // ------------------------------------------------------------------ host dispatch
 
-struct ColsCall {
-    const unsigned char *W;
-    const float *x;
-    int N, K, act;
-    const float *m, *r;
-    float *dst;
-};
+using ColsCall = ColsArgs;
 
 template <int FMT, int NC, int UO> hipError_t launch_cols(const ColsCall &c, hipStream_t s)
 {
@@ -454,7 +453,35 @@ hipError_t dispatch_ncols(int wfmt, int ncols, const ColsCall &c, hipStream_t s)
 } // namespace
 } // namespace gemv
 
+namespace gemv {
+namespace {
+
+// The chunked column kernel's condition (dispatch_cols) for a run-time format.
+bool cols_fast(int wfmt, int64_t K)
+{
+    static const int kE[5] = {4, 8, 8, 16, 32}, kXS[5] = {4, 12, 12, 20, 36};
+    const int64_t rb = wfmt == GEMV_W_F32 ? 4 * K : (wfmt == GEMV_W_Q8B32 ? K : (wfmt == GEMV_W_Q4B32 ? K / 2 : 2 * K));
+    return rb % 16 == 0 && (K / kE[wfmt]) * kXS[wfmt] * 4 <= kMaxLds;
+}
+
+} // namespace
+} // namespace gemv
+
 extern "C" {
+
+int gemv_ncols_kernel(int wfmt, int64_t N, int64_t K, int64_t ncols)
+{
+    if (wfmt < GEMV_W_F32 || wfmt > GEMV_W_Q4B32)
+        return GEMV_E_FMT;
+    if (N < 1 || K < 1 || ncols < 1 || ncols > GEMV_MAX_NCOLS || N >= GEMV_MAX_DIM_EXTENT ||
+        K >= GEMV_MAX_DIM_EXTENT || ((wfmt == GEMV_W_Q8B32 || wfmt == GEMV_W_Q4B32) && K % 32 != 0))
+        return GEMV_E_DIM;
+    if (ncols == 1)
+        return GEMV_KERNEL_ONE_COLUMN;
+    if (GEMV_COLS_MFMA && gemv::cols_mfma_plan(wfmt, (int)ncols, N, K, gemv::device_cus()).rt)
+        return GEMV_KERNEL_COLUMNS_MATRIX;
+    return gemv::cols_fast(wfmt, K) ? GEMV_KERNEL_COLUMNS : GEMV_KERNEL_COLUMNS_GENERIC;
+}
 
 int gemv_fused_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
                      const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst,
@@ -468,6 +495,11 @@ int gemv_fused_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncol
     gemv::ColsCall c{static_cast<const unsigned char *>(W), x, (int)N, (int)K, act,
                      mul_operand ? mul_operand->data : nullptr, add_operand ? add_operand->data : nullptr,
                      dst->data};
+    if (GEMV_COLS_MFMA) {
+        const int e = gemv::launch_cols_mfma(wfmt, (int)ncols, c, hip_stream);
+        if (e >= 0)
+            return gemv::finish_launch(e);
+    }
     return gemv::finish_launch(
         (int)gemv::dispatch_ncols(wfmt, (int)ncols, c, static_cast<hipStream_t>(hip_stream)));
 }

@@ -27,6 +27,26 @@ int validate_fused_fwht(const void *W, int wfmt, int64_t N, int64_t K, const flo
                         int64_t nsigns, int act, const gemv_view *mul_operand, const gemv_view *add_operand,
                         const gemv_view *dst);
 
+// Arguments of one several-column product, checked by validate_ncols.
+struct ColsArgs {
+    const unsigned char *W;
+    const float *x;
+    int N, K, act;
+    const float *m, *r;
+    float *dst;
+};
+
+// The matrix-core column kernel (f16 and block formats).  The plan: tiles of
+// 16 rows per workgroup (rt, 0 where the kernel is not taken), W steps per
+// wave (sw), x octets per builder lane (vo), for a device of `cus` compute
+// units.  launch_cols_mfma launches it on the stream and returns the
+// hipError_t of the launch, or -1 without launching where the plan is empty.
+struct MfmaPlan {
+    int rt, sw, vo;
+};
+MfmaPlan cols_mfma_plan(int wfmt, int ncols, int64_t N, int64_t K, int64_t cus);
+int launch_cols_mfma(int wfmt, int ncols, const ColsArgs &c, void *stream);
+
 // Records a launch's hipError_t as the calling thread's last HIP error and
 // maps it to GEMV_OK or GEMV_E_HIP.
 int finish_launch(int hip_error);

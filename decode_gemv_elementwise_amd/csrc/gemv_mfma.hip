@@ -1,0 +1,544 @@
+// Matrix-core form of the several-column product (ncols = 2..8) for f16
+// weights and the two block formats: dst[b*N + i] = epilogue((W x_b)_i, ...).
+//
+// "feat(cuda): fuse activations and residual add into mmv f/q epilogues",
+// Summary, states the fused matrix-vector path for one destination column.
+// With several columns every weight meets ncols values of x, and on the
+// vector ALUs the multiply-adds, not the bytes, set the time (the 4-bit
+// format crosses over at two columns).  Here the products run on the gfx950
+// matrix cores instead (v_mfma_f32_16x16x32_f16), and the vector ALUs keep
+// only the unpack of the codes and the block scales.
+//
+// Operands of one matrix-core step (32 values of k, 16 rows):
+//  * B (32 x 16) is W: lane n + 16 g holds row n's values k = 32 s + 8 g + p,
+//    p = 0..7, as f16.  f16 weights are the loaded chunk itself; 8-bit codes
+//    and (code - 8) of the 4-bit format are exact in f16.
+//  * A (16 x 32) is x: row m = 2 b + piece of column b.  Each column is scaled
+//    by a power of two 2^(15 - e_b) (e_b the binary exponent of max_k |x_bk|)
+//    and split into hi = f16(x') and lo = f16(2^10 (x' - hi)), both rounded
+//    toward zero: every product with an f16 weight is exact in f32, hi +
+//    2^-10 lo carries x' to 2^-20 relative, and because lo is scaled up the
+//    f16 subnormals only limit values below 2^-48 of the column's largest.
+//    The pieces of every column are built once per workgroup in LDS, in the
+//    A operand's lane layout.
+//  * D (16 x 16): lane n + 16 g' holds row n of pieces 4 g' .. 4 g' + 3, that
+//    is hi and lo of columns 2 g' and 2 g' + 1, so a column is finished
+//    without lane exchange: y = (hi + 2^-10 lo) 2^(e_b - 15).
+// For the block formats every step is one 32-code block: the step's product
+// is scaled by the row's fp16 block scale into a running sum (one FMA per
+// output); f16 weights accumulate in the matrix core across steps.
+//
+// Work layout: a workgroup of 16 waves owns RT tiles of 16 rows.  Waves 8..15
+// build the pieces: each reads a whole column of x (for its maximum) and
+// converts its share of it.  Waves 0..7 split K into KS = 8 / RT slices
+// (wave w: tile w % RT, slice w / RT): they load the epilogue operands, the
+// block scales and W (some of it before the pieces are ready, the rest one
+// load unit ahead of its use), and run the matrix-core steps.  A wave blocks
+// while the memory pipeline is full, so loading W and building the pieces
+// are kept in different waves.  The slices' sums meet in LDS in a fixed
+// order, so the result is deterministic; it differs from the one-column
+// kernel's by rounding only.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "gemv_device.h"
+#include "gemv_internal.h"
+
+namespace gemv {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4))); // x may be 4-byte aligned only
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4u __attribute__((ext_vector_type(4), aligned(4))); // scale runs: 4-byte aligned
+
+constexpr int kMW = 8;      // W and matrix-core waves per workgroup
+constexpr int kWG = 16;     // waves per workgroup: kMW, then 8 builders of the x pieces
+constexpr int kXShift = 15; // a column's largest |x| is scaled into [2^14, 2^15)
+constexpr int kLoShift = 10;
+
+// Slot e of a lane's 8 B values <-> position within its 8 consecutive k (the
+// 4-bit unpack yields the codes of a dword in the order 0, 4, 1, 5, 2, 6, 3, 7).
+template <int FMT> __host__ __device__ constexpr int slot_pos(int e)
+{
+    return FMT == GEMV_W_Q4B32 ? (e >> 1) + 4 * (e & 1) : e;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 q) { return __builtin_bit_cast(f16x8, q); }
+
+// 8 codes of the 4-bit format (element p in bits 4p..4p+3) -> f16 slots
+// (c0-8, c4-8, c1-8, c5-8, c2-8, c6-8, c3-8, c7-8).  A nibble OR-ed into the
+// mantissa of 1024 gives 1024 + c (low nibble) or 1024 + 16 c (high nibble);
+// subtracting 1032, or the fused (1024 + 16 c) / 16 - 72, leaves c - 8
+// exactly, two codes per packed f16 operation.
+__device__ __forceinline__ f16x8 unpack_q4(unsigned d)
+{
+    const f16x2 off1 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const f16x2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const f16x2 off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const unsigned magic = 0x64006400u;
+    const unsigned e = d >> 8;
+    const f16x2 h0 = __builtin_bit_cast(f16x2, and_or(d, 0x000F000Fu, magic)) - off1;
+    const f16x2 h1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, and_or(d, 0x00F000F0u, magic)), k16, off16);
+    const f16x2 h2 = __builtin_bit_cast(f16x2, and_or(e, 0x000F000Fu, magic)) - off1;
+    const f16x2 h3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, and_or(e, 0x00F000F0u, magic)), k16, off16);
+    u32x4 r = {__builtin_bit_cast(unsigned, h0), __builtin_bit_cast(unsigned, h1), __builtin_bit_cast(unsigned, h2),
+               __builtin_bit_cast(unsigned, h3)};
+    return as_f16x8(r);
+}
+
+// 4 int8 codes -> two f16 pairs: byte b ^ 0x80 = c + 128 is OR-ed into the
+// mantissa of 1024 (v_perm places it and the 0x64 exponent byte), and
+// 1152 is subtracted: c exactly.
+__device__ __forceinline__ void unpack_q8(unsigned d, unsigned &lo, unsigned &hi)
+{
+    const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const unsigned u = d ^ 0x80808080u;
+    lo = __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off);
+    hi = __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off);
+}
+
+// 4x4 transpose of dwords across the lane groups g = lane / 16: on entry
+// v[i] of group g is dword i of block g; on exit v[i] of group g is dword g
+// of block i.  permlane32_swap exchanges the upper half of its first operand
+// with the lower half of its second; permlane16_swap the odd 16-lane rows of
+// the first with the even rows of the second.
+__device__ __forceinline__ void transpose4(unsigned (&v)[4])
+{
+    {
+        const auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+        v[0] = a[0];
+        v[2] = a[1];
+        const auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+        v[1] = b[0];
+        v[3] = b[1];
+    }
+    {
+        const auto a = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
+        v[0] = a[0];
+        v[1] = a[1];
+        const auto b = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
+        v[2] = b[0];
+        v[3] = b[1];
+    }
+}
+
+// Lane group G holds dwords 4 G .. 4 G + 3 of a row's two blocks (64 bytes);
+// afterwards v[0..1] of group g are dwords 2 g, 2 g + 1 (block 0) and v[2..3]
+// dwords 8 + 2 g, 9 + 2 g (block 1).  Two 2x2 exchanges: lane-group bit 0
+// with the pair index, then lane-group bit 1 with it.
+__device__ __forceinline__ void permute_q8(unsigned (&v)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const auto a = __builtin_amdgcn_permlane16_swap(v[i], v[i + 2], false, false);
+        v[i] = a[0];
+        v[i + 2] = a[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const auto a = __builtin_amdgcn_permlane32_swap(v[i], v[i + 2], false, false);
+        v[i] = a[0];
+        v[i + 2] = a[1];
+    }
+}
+
+// W of one wave: its 16 rows (lane n + 16 g: row n) over its slice of steps,
+// in load units of 16 bytes per lane.  f16: a unit is one step (lane group
+// g: the step's 8 weights k = 32 s + 8 g ..).  4-bit: a unit is 4 steps
+// (lane group g loads block s + g whole; transpose4 then gives every lane
+// its 8 codes of each of the 4 blocks).  8-bit: a unit is 2 steps (lane
+// group g loads bytes 16 g .. 16 g + 15 of the two blocks; permute_q8).
+// Block scales: units of 8 consecutive fp16 (16 bytes), every lane of a row
+// loading the same ones.
+template <int FMT> constexpr int steps_per_unit() { return FMT == GEMV_W_F16 ? 1 : (FMT == GEMV_W_Q4B32 ? 4 : 2); }
+template <int FMT> constexpr int step_bytes() { return FMT == GEMV_W_F16 ? 64 : (FMT == GEMV_W_Q4B32 ? 16 : 32); }
+
+template <int FMT> constexpr int64_t scale_plane_offset(int64_t N, int64_t K)
+{
+    return align256_dev(N * row_bytes<FMT>(K));
+}
+
+// LDS: [pieces or slice sums][per-wave maxima].  Pieces: piece row m, octet
+// o = 4 s + g (step s, lane group g) -> 16-byte slot m * (K/8 + 1) + o.  The
+// odd row length in slots puts the 16 rows a matrix-core read touches in 16
+// distinct bank groups, and the builders' writes (consecutive octets of one
+// row) are consecutive slots.
+__host__ __device__ constexpr int64_t piece_row_slots(int64_t K) { return K / 8 + 1; }
+template <int NC> __host__ __device__ constexpr int64_t pieces_bytes(int64_t K) { return 2 * NC * piece_row_slots(K) * 16; }
+__host__ __device__ constexpr int64_t mfma_union_bytes(int64_t pb)
+{
+    return pb > kMW * kWave * 16 ? pb : kMW * kWave * 16;
+}
+
+// Steps per wave slice: a whole number of scale units (8 steps) for the
+// block formats.
+__host__ __device__ inline int mfma_spw(int nsteps, int KS, bool block)
+{
+    int spw = (nsteps + KS - 1) / KS;
+    return block ? (spw + 7) & ~7 : spw;
+}
+
+template <int FMT, int NC, int SW, int VO>
+__global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsigned char *W, const float *x, int N,
+                                                                     int K, int RT, int act, const float *mop,
+                                                                     const float *rop, float *dst)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int PC = 2 * NC;    // piece rows of A
+    constexpr int WPC = kMW / NC; // builder waves per column
+    constexpr bool kBlock = Fmt<FMT>::kBlock;
+    constexpr int SPU = steps_per_unit<FMT>();
+    constexpr int NU = SW / SPU;             // W load units per lane
+    // units issued before the pieces are ready (measured per format): f16
+    // has nothing to do meanwhile and issues all; the 4-bit unpack is the
+    // longest, and it overlaps the stream best when most units are issued
+    // one ahead of their use
+    constexpr int PU = FMT == GEMV_W_F16 ? NU : (FMT == GEMV_W_Q4B32 ? NU / 4 : NU / 2);
+    constexpr int NSU = kBlock ? SW / 8 : 1; // scale units per lane
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const bool wwave = w < kMW; // W and matrix-core wave; else a builder
+    const int n = lane & 15, g = lane >> 4;
+    const int nsteps = K / 32;
+    const int KS = kMW / RT;
+    const int t = w % RT, q = (w % kMW) / RT;
+    const int spw = mfma_spw(nsteps, KS, kBlock);
+    const int s0 = q * spw;
+    const int cnt = max(0, min(spw, nsteps - s0));
+    const int row0 = (blockIdx.x * RT + t) * 16;
+    const int row = min(row0 + n, N - 1);
+    const int rs = (int)piece_row_slots(K);
+
+    // builders: the whole of column c (for its maximum), VO octets of 8
+    // values per lane, clamped so that every load is valid; the workgroup
+    // starts at an octet of its own so that the workgroups do not all read
+    // the same lines at once
+    const int c = (w - kMW) % NC, h = (w - kMW) / NC;
+    const int nocts = K / 8;
+    const int rot = (int)(((int64_t)blockIdx.x * kWave) % nocts);
+    float xv[VO][8];
+    if (!wwave) {
+#pragma unroll
+        for (int i = 0; i < VO; ++i) {
+            const int o = (min(lane + kWave * i, nocts - 1) + rot) % nocts;
+            const float *xp = x + (int64_t)c * K + 8 * o;
+            const f32x4u a = *reinterpret_cast<const f32x4u *>(xp);
+            const f32x4u b = *reinterpret_cast<const f32x4u *>(xp + 4);
+            xv[i][0] = a.x, xv[i][1] = a.y, xv[i][2] = a.z, xv[i][3] = a.w;
+            xv[i][4] = b.x, xv[i][5] = b.y, xv[i][6] = b.z, xv[i][7] = b.w;
+        }
+    }
+    // the x loads are queued before any W load
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // W waves: the epilogue operands of this lane's two outputs (row, columns
+    // 2g and 2g + 1; clamped indices, used only where valid), the block
+    // scales and the first PU units of W
+    const float *opnd = (act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL) ? mop : (act == GEMV_ACT_ADD ? rop : nullptr);
+    float ov[2] = {0.0f, 0.0f};
+    const unsigned char *wp = W + (int64_t)row * row_bytes<FMT>(K) + 16 * g;
+    u32x4 wq[NU];
+    u32x4 sq[NSU];
+    float *wmax = reinterpret_cast<float *>(lds + mfma_union_bytes(pieces_bytes<NC>(K)));
+    if (wwave) {
+        if (opnd != nullptr && q == 0) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                ov[u] = opnd[(int64_t)min(2 * g + u, NC - 1) * N + row];
+        }
+        if constexpr (kBlock) {
+            const unsigned char *sp = W + scale_plane_offset<FMT>(N, K) + (int64_t)row * (K / 32) * 2;
+#pragma unroll
+            for (int v = 0; v < NSU; ++v) {
+                const int s = min(s0 + 8 * v, nsteps - 8);
+                sq[v] = *reinterpret_cast<const u32x4u *>(sp + 2 * s);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PU; ++u) {
+            const int s = min(s0 + SPU * u, nsteps - SPU);
+            wq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp + (int64_t)step_bytes<FMT>() * s));
+        }
+    } else if (h < WPC) {
+        // builders: column maximum -> binary exponent, then hi / lo pieces
+        // of this builder's share of the column into the A layout (octet
+        // o is step o / 4, lane group o % 4)
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VO; ++i) {
+            const bool ok = lane + kWave * i < nocts;
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                mx = fmaxf(mx, ok ? fabsf(xv[i][p]) : 0.0f);
+        }
+        mx = wave_max(mx);
+        int ec;
+        (void)frexpf(mx, &ec);
+        const int sh = kXShift - ec;
+        if (lane == 0 && h == 0)
+            wmax[c] = mx;
+        const int opw = (nocts + WPC - 1) / WPC;
+        const int oa = h * opw, ob = min(oa + opw, nocts);
+#pragma unroll
+        for (int i = 0; i < VO; ++i) {
+            const int o = (lane + kWave * i + rot) % nocts;
+            if (lane + kWave * i < nocts && o >= oa && o < ob) {
+                unsigned hw[4], lw[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float v0 = xv[i][slot_pos<FMT>(e)], v1 = xv[i][slot_pos<FMT>(e + 1)];
+                    const f16x2 hp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ldexpf(v0, sh), ldexpf(v1, sh)));
+                    const float r0 = fmaf((float)hp.x, -1024.0f, ldexpf(v0, sh + kLoShift));
+                    const float r1 = fmaf((float)hp.y, -1024.0f, ldexpf(v1, sh + kLoShift));
+                    hw[e / 2] = __builtin_bit_cast(unsigned, hp);
+                    lw[e / 2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+                }
+                u32x4 *slot = reinterpret_cast<u32x4 *>(lds) + 2 * c * rs + o;
+                slot[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                slot[rs] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+
+    // W waves: the slice's steps; unit u + PU is issued before unit u is consumed
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (wwave) {
+        const f16x8 *pa = reinterpret_cast<const f16x8 *>(lds) + (n % PC) * rs + g;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if (u + PU < NU) {
+                const int s = min(s0 + SPU * (u + PU), nsteps - SPU);
+                wq[u + PU] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp + (int64_t)step_bytes<FMT>() * s));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (SPU * u < cnt) {
+                if constexpr (FMT == GEMV_W_F16) {
+                    const f16x8 a = pa[4 * (s0 + u)];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_f16x8(wq[u]), acc, 0, 0, 0);
+                } else {
+                    unsigned d[4] = {wq[u].x, wq[u].y, wq[u].z, wq[u].w};
+                    if constexpr (FMT == GEMV_W_Q4B32)
+                        transpose4(d);
+                    else
+                        permute_q8(d);
+#pragma unroll
+                    for (int i = 0; i < SPU; ++i) {
+                        const int j = SPU * u + i; // step within the slice
+                        f16x8 b;
+                        if constexpr (FMT == GEMV_W_Q4B32) {
+                            b = unpack_q4(d[i]);
+                        } else {
+                            unsigned u0, u1, u2, u3;
+                            unpack_q8(d[2 * i], u0, u1);
+                            unpack_q8(d[2 * i + 1], u2, u3);
+                            b = as_f16x8(u32x4{u0, u1, u2, u3});
+                        }
+                        const f16x8 a = pa[4 * (s0 + j)];
+                        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                        const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, z, 0, 0, 0);
+                        const u32x4 sv = sq[j / 8];
+                        const int k2 = (j % 8) / 2;
+                        const unsigned sd = k2 == 0 ? sv.x : (k2 == 1 ? sv.y : (k2 == 2 ? sv.z : sv.w));
+                        const float scv = (j & 1) ? f16hi(sd) : f16lo(sd);
+                        acc[0] = fmaf(scv, dd[0], acc[0]);
+                        acc[1] = fmaf(scv, dd[1], acc[1]);
+                        acc[2] = fmaf(scv, dd[2], acc[2]);
+                        acc[3] = fmaf(scv, dd[3], acc[3]);
+                    }
+                }
+            }
+        }
+    }
+
+    // slice sums meet in LDS (over the pieces, once every wave is done)
+    lds_barrier();
+    f32x4 *red = reinterpret_cast<f32x4 *>(lds);
+    if (wwave)
+        red[w * kWave + lane] = acc;
+    lds_barrier();
+    if (wwave && q == 0) {
+        f32x4 tot = red[t * kWave + lane];
+        for (int qq = 1; qq < KS; ++qq) {
+            const f32x4 v = red[(t + qq * RT) * kWave + lane];
+            tot[0] += v[0];
+            tot[1] += v[1];
+            tot[2] += v[2];
+            tot[3] += v[3];
+        }
+        const int ro = row0 + n;
+        if (ro < N) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int b = 2 * g + u;
+                if (b < NC) {
+                    int eb;
+                    (void)frexpf(wmax[b], &eb);
+                    const float y = ldexpf(fmaf(tot[2 * u + 1], 1.0f / 1024.0f, tot[2 * u]), eb - kXShift);
+                    dst[(int64_t)b * N + ro] = apply_epilogue(act, y, ov[u]);
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, int NC, int SW, int VO> int launch_mfma(const ColsArgs &c, int RT, hipStream_t s)
+{
+    const void *fn = reinterpret_cast<const void *>(&gemv_cols_mfma_kernel<FMT, NC, SW, VO>);
+    const int64_t lds = mfma_union_bytes(pieces_bytes<NC>(c.K)) + kMW * 4;
+    if (lds > 64 * 1024) {
+        static std::once_flag once;
+        static hipError_t attr_err = hipSuccess;
+        std::call_once(once, [&] { attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds); });
+        if (attr_err != hipSuccess)
+            return (int)attr_err;
+    }
+    const int grid = (c.N + 16 * RT - 1) / (16 * RT);
+    const unsigned char *W = c.W;
+    const float *x = c.x;
+    int N = c.N, K = c.K, rt = RT, act = c.act;
+    const float *m = c.m, *r = c.r;
+    float *dst = c.dst;
+    void *args[] = {&W, &x, &N, &K, &rt, &act, &m, &r, &dst};
+    return (int)hipLaunchKernel(fn, dim3(grid), dim3(kWG * kWave), args, (size_t)lds, s);
+}
+
+// Where the matrix-core kernel is taken instead of the vector-ALU column
+// kernel (measured on the decode shapes).  Its fixed cost (x read and split
+// per workgroup, then the unpack after the pieces are ready) is about 4-6 us
+// over the weight stream, while the vector-ALU kernel's time grows with
+// every column once the multiply-adds outrun the stream.  f16: from five
+// columns.  8-bit: from four where the matrix is 20 MB or more and the
+// tiles make one round of workgroups, from six on 32 MB or more.  4-bit:
+// from three on 16 MB or more, from six on smaller matrices.
+bool mfma_wins(int wfmt, int NC, int64_t tiles, int64_t cus, int64_t wbytes)
+{
+    const int64_t MB = 1 << 20;
+    if (wfmt == GEMV_W_F16)
+        return NC >= 5;
+    if (wfmt == GEMV_W_Q8B32)
+        return (NC >= 4 && wbytes >= 20 * MB && tiles <= cus) || (NC >= 6 && wbytes >= 32 * MB);
+    return NC >= (wbytes >= 16 * MB ? 3 : 6);
+}
+
+int64_t row_bytes_of(int wfmt, int64_t K)
+{
+    return wfmt == GEMV_W_F16 ? 2 * K : (wfmt == GEMV_W_Q8B32 ? K : K / 2);
+}
+
+template <int FMT, int NC, int SW> int launch_mfma_vo(const ColsArgs &c, const MfmaPlan &p, hipStream_t s)
+{
+    if (p.vo <= 4)
+        return launch_mfma<FMT, NC, SW, 4>(c, p.rt, s);
+    if (p.vo <= 8)
+        return launch_mfma<FMT, NC, SW, 8>(c, p.rt, s);
+    return launch_mfma<FMT, NC, SW, 12>(c, p.rt, s);
+}
+
+template <int FMT, int NC> int launch_mfma_plan(const ColsArgs &c, const MfmaPlan &p, hipStream_t s)
+{
+    constexpr int SW1 = Fmt<FMT>::kBlock ? 32 : 16;
+    if constexpr (FMT == GEMV_W_Q4B32) {
+        if (p.sw > SW1)
+            return launch_mfma_vo<FMT, NC, 2 * SW1>(c, p, s);
+    }
+    return launch_mfma_vo<FMT, NC, SW1>(c, p, s);
+}
+
+template <int NC> int launch_mfma_fmt(int wfmt, const ColsArgs &c, const MfmaPlan &p, hipStream_t s)
+{
+    switch (wfmt) {
+    case GEMV_W_F16:
+        return launch_mfma_plan<GEMV_W_F16, NC>(c, p, s);
+    case GEMV_W_Q8B32:
+        return launch_mfma_plan<GEMV_W_Q8B32, NC>(c, p, s);
+    default:
+        return launch_mfma_plan<GEMV_W_Q4B32, NC>(c, p, s);
+    }
+}
+
+} // namespace
+
+// Tiles per workgroup (rt): the fewest that make the grid a single round on
+// the compute units, as long as a W wave's slice fits its registers (sw
+// steps: 16 for f16, which then needs one tile per workgroup; 32 for the
+// 8-bit format; 32 or 64 for the 4-bit format); otherwise fewer.  The shape
+// must also fit: K a whole number of steps (of scale units, 256 values, for
+// the block formats), a column within a builder's registers (K <= 6144),
+// the pieces within LDS.
+MfmaPlan cols_mfma_plan(int wfmt, int ncols, int64_t N, int64_t K, int64_t cus)
+{
+    MfmaPlan p{0, 0, 0};
+    if ((wfmt != GEMV_W_F16 && wfmt != GEMV_W_Q8B32 && wfmt != GEMV_W_Q4B32) || ncols < 2 || ncols > 8 || N < 1)
+        return p;
+    const bool block = wfmt != GEMV_W_F16;
+    if (K < 1 || K % (block ? 256 : 32) != 0 || K > kWave * 8 * 12)
+        return p;
+    if (mfma_union_bytes(2 * ncols * piece_row_slots(K) * 16) + kMW * 4 > kMaxLds)
+        return p;
+    const int64_t tiles = (N + 15) / 16;
+    if (!mfma_wins(wfmt, ncols, tiles, cus, N * row_bytes_of(wfmt, K)))
+        return p;
+    const int sw1 = block ? 32 : 16;
+    const int swmax = wfmt == GEMV_W_Q4B32 ? 64 : sw1;
+    int rt = 1;
+    while (rt < kMW && tiles > cus * rt)
+        rt *= 2;
+    for (; rt >= 1; rt /= 2) {
+        const int spw = mfma_spw((int)(K / 32), kMW / rt, block);
+        if (!block && tiles > cus)
+            break;
+        if (spw <= swmax) {
+            p.rt = rt;
+            p.sw = spw <= sw1 ? sw1 : swmax;
+            break;
+        }
+    }
+    if (p.rt) {
+        const int64_t vo = (K / 8 + kWave - 1) / kWave; // x octets per builder lane
+        p.vo = vo <= 4 ? 4 : (vo <= 8 ? 8 : 12);
+    }
+    return p;
+}
+
+int launch_cols_mfma(int wfmt, int ncols, const ColsArgs &c, void *stream)
+{
+    const MfmaPlan p = cols_mfma_plan(wfmt, ncols, c.N, c.K, device_cus());
+    if (!p.rt)
+        return -1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (ncols) {
+    case 2:
+        return launch_mfma_fmt<2>(wfmt, c, p, s);
+    case 3:
+        return launch_mfma_fmt<3>(wfmt, c, p, s);
+    case 4:
+        return launch_mfma_fmt<4>(wfmt, c, p, s);
+    case 5:
+        return launch_mfma_fmt<5>(wfmt, c, p, s);
+    case 6:
+        return launch_mfma_fmt<6>(wfmt, c, p, s);
+    case 7:
+        return launch_mfma_fmt<7>(wfmt, c, p, s);
+    default:
+        return launch_mfma_fmt<8>(wfmt, c, p, s);
+    }
+}
+
+} // namespace gemv

@@ -184,14 +184,34 @@ int gemv_glu_validate(const void *W_gate, const void *W_up, int wfmt, int64_t N,
  *              as [ncols, N] or [ncols, 32, 128]); operand rules, the in-place
  *              case and the overlap rule are those of gemv_fused, with x
  *              spanning ncols * K floats.
- * Column b of the result is bit for bit the gemv_fused result for x_b and
- * operand row b whenever K meets the fast-path conditions (K a multiple of
- * the 16-byte chunk: 4 f32, 8 f16/bf16 values; always for block formats);
- * ncols == 1 is gemv_fused itself.  Returns GEMV_OK or a negative status;
- * asynchronous on hip_stream; allocates nothing. */
+ * Kernels (gemv_ncols_kernel names the one a call takes): f32 and bf16, and
+ * f16 and the block formats at few columns, run a vector-ALU column kernel
+ * whose column b is bit for bit the gemv_fused result for x_b and operand
+ * row b whenever K meets the fast-path conditions (K a multiple of the
+ * 16-byte chunk: 4 f32, 8 f16/bf16 values; always for block formats).  f16
+ * and the block formats at more columns run on the matrix cores: there x is
+ * carried as two f16 pieces per value (to 2^-20 relative, below 2^-48 of
+ * the column's largest |x| absolutely), the result agrees with gemv_fused
+ * within the format's tolerance, and each column is independent of the
+ * others bit for bit.  ncols == 1 is gemv_fused itself.  Returns GEMV_OK or
+ * a negative status; asynchronous on hip_stream; allocates nothing. */
 int gemv_fused_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
                      const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst,
                      void *hip_stream);
+
+/* The kernel gemv_fused_ncols launches for a format and shape on the current
+ * device (the choice depends on the device's compute-unit count, which is
+ * queried once per device).  Not part of any computation: for tests,
+ * benchmarks and tuning.  Returns a gemv_kernel value, or GEMV_E_FMT /
+ * GEMV_E_DIM for arguments gemv_fused_ncols would reject on those grounds
+ * (ncols == 1 needs no HIP call). */
+typedef enum {
+    GEMV_KERNEL_ONE_COLUMN = 1,      /* gemv_fused's kernels (ncols == 1) */
+    GEMV_KERNEL_COLUMNS = 2,         /* vector-ALU column kernel, 16-byte chunks */
+    GEMV_KERNEL_COLUMNS_GENERIC = 3, /* vector-ALU column kernel, element loads */
+    GEMV_KERNEL_COLUMNS_MATRIX = 4   /* matrix-core column kernel */
+} gemv_kernel;
+int gemv_ncols_kernel(int wfmt, int64_t N, int64_t K, int64_t ncols);
 
 /* The host-side checks of gemv_fused_ncols; no HIP call. */
 int gemv_fused_ncols_validate(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x,

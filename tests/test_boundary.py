@@ -300,3 +300,16 @@ def test_fused_fwht_validate():
     # the gemv_fused checks come first
     assert ffval(act="add", add_operand=None) == S["GEMV_E_OPERAND"]
     assert ffval(dst=v(X0, (64,))) == S["GEMV_E_ALIAS"]
+
+
+def test_ncols_kernel_query_arguments():
+    """The query needs no device for rejected arguments or one column."""
+    assert b.gemv_ncols_kernel("f16", 64, 64, 1) == "one_column"
+    assert b.gemv_ncols_kernel("q4b32", 4096, 4096, 1) == "one_column"
+    for args, code in [(("f16", 0, 64, 2), "GEMV_E_DIM"), (("f16", 64, 0, 2), "GEMV_E_DIM"),
+                       (("f16", 64, 64, 9), "GEMV_E_DIM"), (("f16", 64, 64, 0), "GEMV_E_DIM"),
+                       (("q8b32", 64, 48, 2), "GEMV_E_DIM"), (("q4b32", 64, 1 << 31, 2), "GEMV_E_DIM")]:
+        with pytest.raises(b.GemvError) as e:
+            b.gemv_ncols_kernel(*args)
+        assert e.value.status == S[code], args
+    assert b.load().gemv_ncols_kernel(9, 64, 64, 2) == S["GEMV_E_FMT"]

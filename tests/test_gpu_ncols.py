@@ -1,6 +1,8 @@
 """GPU parity of gemv_fused_ncols (2..8 destination columns over one W)
-against the oracle, and its bit-for-bit agreement with one gemv_fused call per
-column."""
+against the oracle.  f32 and bf16 columns (vector-ALU column kernel) also
+equal one gemv_fused call per column bit for bit; f16 and the block formats
+run on the matrix cores where the shape fits, and there every column is
+independent of its position among the others, bit for bit."""
 import zlib
 
 import numpy as np
@@ -68,7 +70,7 @@ def _one_column(w, x, act, m, r):
     return host(dst).copy()
 
 
-@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
 @pytest.mark.parametrize("N,K,act", [(300, 4096, "silu_mul"), (67, 14336, "add"), (17, 4128, "sigmoid"),
                                      (40, 96, "mul")])
 def test_ncols_columns_equal_one_column_calls_bitwise(fmt, N, K, act):
@@ -82,6 +84,24 @@ def test_ncols_columns_equal_one_column_calls_bitwise(fmt, N, K, act):
     for b in range(B):
         one = _one_column(w, X[b], act, None if M is None else M[b], None if R is None else R[b])
         assert np.array_equal(g[b].view(np.uint32), one.view(np.uint32)), (fmt, b)
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("N,K,B,act", [(300, 4096, 8, "silu_mul"), (67, 14336, 3, "add"), (17, 4128, 5, "sigmoid"),
+                                       (40, 96, 2, "mul"), (5000, 1024, 4, "add"), (4100, 2048, 7, "silu")])
+def test_ncols_columns_independent_of_position_bitwise(fmt, N, K, B, act):
+    """Rolling the columns of x (and of the operands) rolls the result
+    columns, bit for bit, on every path."""
+    rng = np.random.default_rng(N + K + 99)
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(B, K)).astype(np.float32)
+    M, R = _operands(rng, act, B, N)
+    log(f"ncols position fmt={fmt} N={N} K={K} B={B} act={act}")
+    g = check_ncols(w, X, act, M, R, tag="position").reshape(B, N)
+    for sft in range(1, B):
+        roll = lambda a: None if a is None else np.roll(a, -sft, axis=0)
+        g2 = run_ncols(w, roll(X), act, roll(M), roll(R)).reshape(B, N)
+        assert np.array_equal(g2.view(np.uint32), np.roll(g, -sft, axis=0).view(np.uint32)), (fmt, sft)
 
 
 def test_ncols_odd_k_columns_equal_one_column_calls_bitwise():
@@ -114,7 +134,8 @@ def test_ncols_inplace_and_view():
 
 
 @pytest.mark.parametrize("fmt,N,K,act", [("q4b32", 14336, 4096, "silu"), ("bf16", 14336, 4096, "silu_mul"),
-                                         ("f16", 4096, 4096, "add"), ("q4b32", 4096, 14336, "add")])
+                                         ("f16", 4096, 4096, "add"), ("q4b32", 4096, 14336, "add"),
+                                         ("q8b32", 14336, 4096, "mul")])
 def test_ncols_full_size(fmt, N, K, act):
     rng = np.random.default_rng(8)
     w = synth.random_weights(rng, fmt, N, K)
@@ -149,12 +170,13 @@ def test_ncols_rejected_call_writes_nothing():
     assert torch.all(dst == 7.0)
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "q4b32"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "f16", "q4b32"])
 def test_ncols_x_not_16_byte_aligned(fmt):
-    """x at a 4-byte (not 16-byte) aligned address: the x copies into LDS go a
-    dword at a time; columns still equal the one-column calls bit for bit."""
+    """x at a 4-byte (not 16-byte) aligned address: the result equals the
+    same call with 16-byte aligned x bit for bit, and for f32/bf16 the
+    one-column calls too."""
     rng = np.random.default_rng(11)
-    N, K, B = 200, 2048, 5
+    N, K, B = 200, 2048, 6
     w = synth.random_weights(rng, fmt, N, K)
     X = rng.normal(size=(B, K)).astype(np.float32)
     Wd = dev(w.data)
@@ -170,8 +192,47 @@ def test_ncols_x_not_16_byte_aligned(fmt):
     Y, acc, absacc = oracle.ncols_reference(fmt, N, K, w.data, X, "silu")
     res = compare(g.reshape(-1), Y.reshape(-1), acc.reshape(-1), absacc.reshape(-1), "silu")
     assert res["max_err"] <= TOLERANCE[fmt], res
-    for b in range(B):
-        one = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
-        binding.gemv_fused(Wd, fmt, N, K, xv[b * K:(b + 1) * K], "silu", dst=one)
-        torch.cuda.synchronize()
-        assert np.array_equal(g[b].view(np.uint32), host(one).view(np.uint32)), b
+    aligned = run_ncols(w, X, "silu").reshape(B, N)
+    assert np.array_equal(g.view(np.uint32), aligned.view(np.uint32))
+    if fmt in ("f32", "bf16"):
+        for b in range(B):
+            one = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+            binding.gemv_fused(Wd, fmt, N, K, xv[b * K:(b + 1) * K], "silu", dst=one)
+            torch.cuda.synchronize()
+            assert np.array_equal(g[b].view(np.uint32), host(one).view(np.uint32)), b
+
+
+@pytest.mark.parametrize("fmt", ["f16", "q8b32", "q4b32"])
+@pytest.mark.parametrize("N,K", [(300, 4096), (4500, 1024)])
+def test_ncols_wide_range_columns(fmt, N, K):
+    """Columns far apart in magnitude (each column takes its own power-of-two
+    scale on the matrix-core path), a zero column, a column with one large
+    value among tiny ones, a subnormal column: each within tolerance, the
+    zero column exactly epilogue(0)."""
+    rng = np.random.default_rng(N + K + 12)
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(6, K)).astype(np.float32)
+    X[0] *= np.float32(1e30)
+    X[1] *= np.float32(1e-30)
+    X[2] = 0.0
+    X[3] *= np.float32(1e-4)
+    X[3, K // 3] = 1e4
+    X[4] = (X[4] * np.float32(1e-40)).astype(np.float32)
+    X[5] *= np.float32(3e4)
+    g = check_ncols(w, X, "add", R=rng.normal(size=(6, N)).astype(np.float32), tag="wide range").reshape(6, N)
+    g0 = check_ncols(w, X, "sigmoid", tag="wide range sigmoid").reshape(6, N)
+    assert np.all(g0[2] == 0.5)
+
+
+@pytest.mark.parametrize("fmt,N,K,ncols,kernel", [
+    ("f16", 4096, 4096, 8, "columns_matrix"), ("f16", 300, 4096, 5, "columns_matrix"),
+    ("f16", 4096, 4096, 4, "columns"), ("f16", 14336, 4096, 8, "columns"),
+    ("q4b32", 14336, 4096, 4, "columns_matrix"), ("q4b32", 14336, 4096, 8, "columns_matrix"),
+    ("q4b32", 300, 4096, 8, "columns_matrix"), ("q4b32", 4100, 2048, 7, "columns_matrix"),
+    ("q4b32", 4096, 4096, 2, "columns"), ("q4b32", 4096, 14336, 8, "columns"), ("q4b32", 33, 96, 8, "columns"),
+    ("q8b32", 4096, 6144, 4, "columns_matrix"), ("q8b32", 14336, 4096, 8, "columns_matrix"),
+    ("q8b32", 4096, 6144, 8, "columns"), ("q8b32", 4096, 4096, 4, "columns"),
+    ("bf16", 4096, 4096, 8, "columns"), ("f32", 64, 1001, 4, "columns_generic"), ("f16", 64, 64, 1, "one_column")])
+def test_ncols_kernel_choice(fmt, N, K, ncols, kernel):
+    """The shapes the tests above rely on to reach each kernel take it."""
+    assert binding.gemv_ncols_kernel(fmt, N, K, ncols) == kernel
