@@ -1,32 +1,36 @@
-// Matrix-core form of the several-column product (ncols = 2..8) for f16
-// weights and the two block formats: dst[b*N + i] = epilogue((W x_b)_i, ...).
+// Matrix-core form of the several-column product (ncols = 2..8) for the
+// 16-bit and the block formats: dst[b*N + i] = epilogue((W x_b)_i, ...).
 //
 // "feat(cuda): fuse activations and residual add into mmv f/q epilogues",
 // Summary, states the fused matrix-vector path for one destination column.
 // With several columns every weight meets ncols values of x, and on the
 // vector ALUs the multiply-adds, not the bytes, set the time (the 4-bit
 // format crosses over at two columns).  Here the products run on the gfx950
-// matrix cores instead (v_mfma_f32_16x16x32_f16), and the vector ALUs keep
-// only the unpack of the codes and the block scales.
+// matrix cores instead (v_mfma_f32_16x16x32_f16, _bf16 for bf16 weights),
+// and the vector ALUs keep only the unpack of the codes and the block scales.
 //
 // Operands of one matrix-core step (32 values of k, 16 rows):
 //  * B (32 x 16) is W: lane n + 16 g holds row n's values k = 32 s + 8 g + p,
-//    p = 0..7, as f16.  f16 weights are the loaded chunk itself; 8-bit codes
-//    and (code - 8) of the 4-bit format are exact in f16.
-//  * A (16 x 32) is x: row m = 2 b + piece of column b.  Each column is scaled
-//    by a power of two 2^(15 - e_b) (e_b the binary exponent of max_k |x_bk|)
-//    and split into hi = f16(x') and lo = f16(2^10 (x' - hi)), both rounded
-//    toward zero: every product with an f16 weight is exact in f32, hi +
-//    2^-10 lo carries x' to 2^-20 relative, and because lo is scaled up the
-//    f16 subnormals only limit values below 2^-48 of the column's largest.
-//    The pieces of every column are built once per workgroup in LDS, in the
-//    A operand's lane layout.
+//    p = 0..7, as f16 (bf16).  16-bit weights are the loaded chunk itself;
+//    8-bit codes and (code - 8) of the 4-bit format are exact in f16.
+//  * A (16 x 32) is x: row m = 2 b + piece of column b.  For the f16 MFMA
+//    each column is scaled by a power of two 2^(15 - e_b) (e_b the binary
+//    exponent of max_k |x_bk|) and split into hi = f16(x') and
+//    lo = f16(2^10 (x' - hi)), both rounded toward zero: every product with
+//    an f16 weight is exact in f32, hi + 2^-10 lo carries x' to 2^-20
+//    relative, and because lo is scaled up the f16 subnormals only limit
+//    values below 2^-48 of the column's largest.  For the bf16 MFMA, hi is
+//    the upper half of x and lo that of x - hi (2^-15 relative; bf16 has the
+//    exponent range of f32, so nothing is scaled).  The pieces of every
+//    column are built once per workgroup in LDS, in the A operand's lane
+//    layout.
 //  * D (16 x 16): lane n + 16 g' holds row n of pieces 4 g' .. 4 g' + 3, that
 //    is hi and lo of columns 2 g' and 2 g' + 1, so a column is finished
-//    without lane exchange: y = (hi + 2^-10 lo) 2^(e_b - 15).
+//    without lane exchange: y = (hi + 2^-10 lo) 2^(e_b - 15) (hi + lo for
+//    bf16).
 // For the block formats every step is one 32-code block: the step's product
 // is scaled by the row's fp16 block scale into a running sum (one FMA per
-// output); f16 weights accumulate in the matrix core across steps.
+// output); 16-bit weights accumulate in the matrix core across steps.
 //
 // Work layout: a workgroup of 16 waves owns RT tiles of 16 rows.  Waves 8..15
 // build the pieces: each reads a whole column of x (for its maximum) and
@@ -51,6 +55,7 @@ namespace gemv {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4))); // x may be 4-byte aligned only
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4u __attribute__((ext_vector_type(4), aligned(4))); // scale runs: 4-byte aligned
@@ -163,8 +168,9 @@ __device__ __forceinline__ void permute_q8(unsigned (&v)[4])
 // group g loads bytes 16 g .. 16 g + 15 of the two blocks; permute_q8).
 // Block scales: units of 8 consecutive fp16 (16 bytes), every lane of a row
 // loading the same ones.
-template <int FMT> constexpr int steps_per_unit() { return FMT == GEMV_W_F16 ? 1 : (FMT == GEMV_W_Q4B32 ? 4 : 2); }
-template <int FMT> constexpr int step_bytes() { return FMT == GEMV_W_F16 ? 64 : (FMT == GEMV_W_Q4B32 ? 16 : 32); }
+template <int FMT> constexpr bool is16() { return FMT == GEMV_W_F16 || FMT == GEMV_W_BF16; }
+template <int FMT> constexpr int steps_per_unit() { return is16<FMT>() ? 1 : (FMT == GEMV_W_Q4B32 ? 4 : 2); }
+template <int FMT> constexpr int step_bytes() { return is16<FMT>() ? 64 : (FMT == GEMV_W_Q4B32 ? 16 : 32); }
 
 template <int FMT> constexpr int64_t scale_plane_offset(int64_t N, int64_t K)
 {
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
     // has nothing to do meanwhile and issues all; the 4-bit unpack is the
     // longest, and it overlaps the stream best when most units are issued
     // one ahead of their use
-    constexpr int PU = FMT == GEMV_W_F16 ? NU : (FMT == GEMV_W_Q4B32 ? NU / 4 : NU / 2);
+    constexpr int PU = is16<FMT>() ? NU : (FMT == GEMV_W_Q4B32 ? NU / 4 : NU / 2);
     constexpr int NSU = kBlock ? SW / 8 : 1; // scale units per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -274,6 +280,30 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
             const int s = min(s0 + SPU * u, nsteps - SPU);
             wq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp + (int64_t)step_bytes<FMT>() * s));
         }
+    } else if (FMT == GEMV_W_BF16 && h < WPC) {
+        // builders (bf16 weights): x = hi + lo with hi the upper 16 bits of x
+        // and lo those of x - hi (exact in f32), both bf16; no scaling, since
+        // bf16 has the exponent range of f32
+        const int opw = (nocts + WPC - 1) / WPC;
+        const int oa = h * opw, ob = min(oa + opw, nocts);
+#pragma unroll
+        for (int i = 0; i < VO; ++i) {
+            const int o = (lane + kWave * i + rot) % nocts;
+            if (lane + kWave * i < nocts && o >= oa && o < ob) {
+                unsigned hw[4], lw[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const unsigned b0 = __builtin_bit_cast(unsigned, xv[i][e]), b1 = __builtin_bit_cast(unsigned, xv[i][e + 1]);
+                    const float r0 = xv[i][e] - __builtin_bit_cast(float, b0 & 0xFFFF0000u);
+                    const float r1 = xv[i][e + 1] - __builtin_bit_cast(float, b1 & 0xFFFF0000u);
+                    hw[e / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+                    lw[e / 2] = __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, r1), __builtin_bit_cast(unsigned, r0), 0x07060302u);
+                }
+                u32x4 *slot = reinterpret_cast<u32x4 *>(lds) + 2 * c * rs + o;
+                slot[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                slot[rs] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+            }
+        }
     } else if (h < WPC) {
         // builders: column maximum -> binary exponent, then hi / lo pieces
         // of this builder's share of the column into the A layout (octet
@@ -320,7 +350,7 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
     // W waves: the slice's steps; unit u + PU is issued before unit u is consumed
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (wwave) {
-        const f16x8 *pa = reinterpret_cast<const f16x8 *>(lds) + (n % PC) * rs + g;
+        const u32x4 *pa = reinterpret_cast<const u32x4 *>(lds) + (n % PC) * rs + g;
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             if (u + PU < NU) {
@@ -330,8 +360,11 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
             __builtin_amdgcn_sched_barrier(0);
             if (SPU * u < cnt) {
                 if constexpr (FMT == GEMV_W_F16) {
-                    const f16x8 a = pa[4 * (s0 + u)];
+                    const f16x8 a = as_f16x8(pa[4 * (s0 + u)]);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_f16x8(wq[u]), acc, 0, 0, 0);
+                } else if constexpr (FMT == GEMV_W_BF16) {
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, pa[4 * (s0 + u)]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, wq[u]), acc, 0, 0, 0);
                 } else {
                     unsigned d[4] = {wq[u].x, wq[u].y, wq[u].z, wq[u].w};
                     if constexpr (FMT == GEMV_W_Q4B32)
@@ -350,7 +383,7 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
                             unpack_q8(d[2 * i + 1], u2, u3);
                             b = as_f16x8(u32x4{u0, u1, u2, u3});
                         }
-                        const f16x8 a = pa[4 * (s0 + j)];
+                        const f16x8 a = as_f16x8(pa[4 * (s0 + j)]);
                         const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
                         const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, z, 0, 0, 0);
                         const u32x4 sv = sq[j / 8];
@@ -388,9 +421,14 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
             for (int u = 0; u < 2; ++u) {
                 const int b = 2 * g + u;
                 if (b < NC) {
-                    int eb;
-                    (void)frexpf(wmax[b], &eb);
-                    const float y = ldexpf(fmaf(tot[2 * u + 1], 1.0f / 1024.0f, tot[2 * u]), eb - kXShift);
+                    float y;
+                    if constexpr (FMT == GEMV_W_BF16) {
+                        y = tot[2 * u] + tot[2 * u + 1];
+                    } else {
+                        int eb;
+                        (void)frexpf(wmax[b], &eb);
+                        y = ldexpf(fmaf(tot[2 * u + 1], 1.0f / 1024.0f, tot[2 * u]), eb - kXShift);
+                    }
                     dst[(int64_t)b * N + ro] = apply_epilogue(act, y, ov[u]);
                 }
             }
@@ -423,15 +461,16 @@ template <int FMT, int NC, int SW, int VO> int launch_mfma(const ColsArgs &c, in
 // kernel (measured on the decode shapes).  Its fixed cost (x read and split
 // per workgroup, then the unpack after the pieces are ready) is about 4-6 us
 // over the weight stream, while the vector-ALU kernel's time grows with
-// every column once the multiply-adds outrun the stream.  f16: from five
-// columns.  8-bit: from four where the matrix is 20 MB or more and the
-// tiles make one round of workgroups, from six on 32 MB or more.  4-bit:
-// from three on 16 MB or more, from six on smaller matrices.
-bool mfma_wins(int wfmt, int NC, int64_t tiles, int64_t cus, int64_t wbytes)
+// every column once the multiply-adds outrun the stream.  f16/bf16: from
+// five columns where K >= 4096, from seven on shorter rows.  8-bit: from
+// four where the matrix is 20 MB or more and the tiles make one round of
+// workgroups, from six on 32 MB or more.  4-bit: from three on 16 MB or
+// more, from six on smaller matrices.
+bool mfma_wins(int wfmt, int NC, int64_t K, int64_t tiles, int64_t cus, int64_t wbytes)
 {
     const int64_t MB = 1 << 20;
-    if (wfmt == GEMV_W_F16)
-        return NC >= 5;
+    if (wfmt == GEMV_W_F16 || wfmt == GEMV_W_BF16)
+        return NC >= (K >= 4096 ? 5 : 7);
     if (wfmt == GEMV_W_Q8B32)
         return (NC >= 4 && wbytes >= 20 * MB && tiles <= cus) || (NC >= 6 && wbytes >= 32 * MB);
     return NC >= (wbytes >= 16 * MB ? 3 : 6);
@@ -439,7 +478,7 @@ bool mfma_wins(int wfmt, int NC, int64_t tiles, int64_t cus, int64_t wbytes)
 
 int64_t row_bytes_of(int wfmt, int64_t K)
 {
-    return wfmt == GEMV_W_F16 ? 2 * K : (wfmt == GEMV_W_Q8B32 ? K : K / 2);
+    return (wfmt == GEMV_W_F16 || wfmt == GEMV_W_BF16) ? 2 * K : (wfmt == GEMV_W_Q8B32 ? K : K / 2);
 }
 
 template <int FMT, int NC, int SW> int launch_mfma_vo(const ColsArgs &c, const MfmaPlan &p, hipStream_t s)
@@ -466,6 +505,8 @@ template <int NC> int launch_mfma_fmt(int wfmt, const ColsArgs &c, const MfmaPla
     switch (wfmt) {
     case GEMV_W_F16:
         return launch_mfma_plan<GEMV_W_F16, NC>(c, p, s);
+    case GEMV_W_BF16:
+        return launch_mfma_plan<GEMV_W_BF16, NC>(c, p, s);
     case GEMV_W_Q8B32:
         return launch_mfma_plan<GEMV_W_Q8B32, NC>(c, p, s);
     default:
@@ -477,7 +518,7 @@ template <int NC> int launch_mfma_fmt(int wfmt, const ColsArgs &c, const MfmaPla
 
 // Tiles per workgroup (rt): the fewest that make the grid a single round on
 // the compute units, as long as a W wave's slice fits its registers (sw
-// steps: 16 for f16, which then needs one tile per workgroup; 32 for the
+// steps: 16 for f16/bf16, which then need one tile per workgroup; 32 for the
 // 8-bit format; 32 or 64 for the 4-bit format); otherwise fewer.  The shape
 // must also fit: K a whole number of steps (of scale units, 256 values, for
 // the block formats), a column within a builder's registers (K <= 6144),
@@ -485,15 +526,15 @@ template <int NC> int launch_mfma_fmt(int wfmt, const ColsArgs &c, const MfmaPla
 MfmaPlan cols_mfma_plan(int wfmt, int ncols, int64_t N, int64_t K, int64_t cus)
 {
     MfmaPlan p{0, 0, 0};
-    if ((wfmt != GEMV_W_F16 && wfmt != GEMV_W_Q8B32 && wfmt != GEMV_W_Q4B32) || ncols < 2 || ncols > 8 || N < 1)
+    if (wfmt == GEMV_W_F32 || wfmt < 0 || wfmt > GEMV_W_Q4B32 || ncols < 2 || ncols > 8 || N < 1)
         return p;
-    const bool block = wfmt != GEMV_W_F16;
+    const bool block = wfmt == GEMV_W_Q8B32 || wfmt == GEMV_W_Q4B32;
     if (K < 1 || K % (block ? 256 : 32) != 0 || K > kWave * 8 * 12)
         return p;
     if (mfma_union_bytes(2 * ncols * piece_row_slots(K) * 16) + kMW * 4 > kMaxLds)
         return p;
     const int64_t tiles = (N + 15) / 16;
-    if (!mfma_wins(wfmt, ncols, tiles, cus, N * row_bytes_of(wfmt, K)))
+    if (!mfma_wins(wfmt, ncols, K, tiles, cus, N * row_bytes_of(wfmt, K)))
         return p;
     const int sw1 = block ? 32 : 16;
     const int swmax = wfmt == GEMV_W_Q4B32 ? 64 : sw1;

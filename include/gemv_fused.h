@@ -184,17 +184,19 @@ int gemv_glu_validate(const void *W_gate, const void *W_up, int wfmt, int64_t N,
  *              as [ncols, N] or [ncols, 32, 128]); operand rules, the in-place
  *              case and the overlap rule are those of gemv_fused, with x
  *              spanning ncols * K floats.
- * Kernels (gemv_ncols_kernel names the one a call takes): f32 and bf16, and
- * f16 and the block formats at few columns, run a vector-ALU column kernel
- * whose column b is bit for bit the gemv_fused result for x_b and operand
- * row b whenever K meets the fast-path conditions (K a multiple of the
- * 16-byte chunk: 4 f32, 8 f16/bf16 values; always for block formats).  f16
- * and the block formats at more columns run on the matrix cores: there x is
- * carried as two f16 pieces per value (to 2^-20 relative, below 2^-48 of
- * the column's largest |x| absolutely), the result agrees with gemv_fused
- * within the format's tolerance, and each column is independent of the
- * others bit for bit.  ncols == 1 is gemv_fused itself.  Returns GEMV_OK or
- * a negative status; asynchronous on hip_stream; allocates nothing. */
+ * Kernels (gemv_ncols_kernel names the one a call takes): f32, and the
+ * other formats at few columns, run a vector-ALU column kernel whose column
+ * b is bit for bit the gemv_fused result for x_b and operand row b whenever
+ * K meets the fast-path conditions (K a multiple of the 16-byte chunk: 4
+ * f32, 8 f16/bf16 values; always for block formats).  The 16-bit and block
+ * formats at more columns run on the matrix cores: there x is carried as
+ * two 16-bit pieces per value (f16 pieces of the column scaled by a power
+ * of two: 2^-20 relative, and below 2^-48 of the column's largest |x|
+ * absolutely; bf16 pieces for bf16 weights: 2^-15 relative), the result
+ * agrees with gemv_fused within the format's tolerance, and each column is
+ * independent of the others bit for bit.  ncols == 1 is gemv_fused itself.
+ * Returns GEMV_OK or a negative status; asynchronous on hip_stream;
+ * allocates nothing. */
 int gemv_fused_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
                      const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst,
                      void *hip_stream);

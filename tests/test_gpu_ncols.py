@@ -70,13 +70,15 @@ def _one_column(w, x, act, m, r):
     return host(dst).copy()
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", synth.FORMATS)
 @pytest.mark.parametrize("N,K,act", [(300, 4096, "silu_mul"), (67, 14336, "add"), (17, 4128, "sigmoid"),
                                      (40, 96, "mul")])
 def test_ncols_columns_equal_one_column_calls_bitwise(fmt, N, K, act):
+    """On the vector-ALU column kernel (f32 at 8 columns, every format at 2)."""
     rng = np.random.default_rng(N + K + 77)
     w = synth.random_weights(rng, fmt, N, K)
-    B = 8
+    B = 8 if fmt == "f32" else 2
+    assert binding.gemv_ncols_kernel(fmt, N, K, B) != "columns_matrix"
     X = rng.normal(size=(B, K)).astype(np.float32)
     M, R = _operands(rng, act, B, N)
     log(f"ncols-vs-one-column fmt={fmt} N={N} K={K} act={act}")
@@ -173,8 +175,8 @@ def test_ncols_rejected_call_writes_nothing():
 @pytest.mark.parametrize("fmt", ["f32", "bf16", "f16", "q4b32"])
 def test_ncols_x_not_16_byte_aligned(fmt):
     """x at a 4-byte (not 16-byte) aligned address: the result equals the
-    same call with 16-byte aligned x bit for bit, and for f32/bf16 the
-    one-column calls too."""
+    same call with 16-byte aligned x bit for bit, and on the vector-ALU
+    kernel (f32 here) the one-column calls too."""
     rng = np.random.default_rng(11)
     N, K, B = 200, 2048, 6
     w = synth.random_weights(rng, fmt, N, K)
@@ -194,7 +196,7 @@ def test_ncols_x_not_16_byte_aligned(fmt):
     assert res["max_err"] <= TOLERANCE[fmt], res
     aligned = run_ncols(w, X, "silu").reshape(B, N)
     assert np.array_equal(g.view(np.uint32), aligned.view(np.uint32))
-    if fmt in ("f32", "bf16"):
+    if binding.gemv_ncols_kernel(fmt, N, K, B) != "columns_matrix":
         for b in range(B):
             one = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
             binding.gemv_fused(Wd, fmt, N, K, xv[b * K:(b + 1) * K], "silu", dst=one)
@@ -202,7 +204,7 @@ def test_ncols_x_not_16_byte_aligned(fmt):
             assert np.array_equal(g[b].view(np.uint32), host(one).view(np.uint32)), b
 
 
-@pytest.mark.parametrize("fmt", ["f16", "q8b32", "q4b32"])
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "q8b32", "q4b32"])
 @pytest.mark.parametrize("N,K", [(300, 4096), (4500, 1024)])
 def test_ncols_wide_range_columns(fmt, N, K):
     """Columns far apart in magnitude (each column takes its own power-of-two
@@ -232,7 +234,9 @@ def test_ncols_wide_range_columns(fmt, N, K):
     ("q4b32", 4096, 4096, 2, "columns"), ("q4b32", 4096, 14336, 8, "columns"), ("q4b32", 33, 96, 8, "columns"),
     ("q8b32", 4096, 6144, 4, "columns_matrix"), ("q8b32", 14336, 4096, 8, "columns_matrix"),
     ("q8b32", 4096, 6144, 8, "columns"), ("q8b32", 4096, 4096, 4, "columns"),
-    ("bf16", 4096, 4096, 8, "columns"), ("f32", 64, 1001, 4, "columns_generic"), ("f16", 64, 64, 1, "one_column")])
+    ("bf16", 4096, 4096, 8, "columns_matrix"), ("bf16", 4096, 4096, 4, "columns"), ("bf16", 14336, 4096, 8, "columns"),
+    ("bf16", 4096, 2048, 6, "columns"), ("bf16", 4096, 2048, 8, "columns_matrix"),
+    ("f32", 4096, 4096, 8, "columns"), ("f32", 64, 1001, 4, "columns_generic"), ("f16", 64, 64, 1, "one_column")])
 def test_ncols_kernel_choice(fmt, N, K, ncols, kernel):
     """The shapes the tests above rely on to reach each kernel take it."""
     assert binding.gemv_ncols_kernel(fmt, N, K, ncols) == kernel
