@@ -36,13 +36,15 @@ struct ColsArgs {
     float *dst;
 };
 
-// The matrix-core column kernel (f16 and block formats).  The plan: tiles of
-// 16 rows per workgroup (rt, 0 where the kernel is not taken), W steps per
-// wave (sw), x octets per builder lane (vo), for a device of `cus` compute
-// units.  launch_cols_mfma launches it on the stream and returns the
-// hipError_t of the launch, or -1 without launching where the plan is empty.
+// The matrix-core column kernels (16-bit and block formats).  The plan: tiles
+// of 16 rows per workgroup (rt, 0 where the kernels are not taken), W steps
+// per wave (sw; per wave and segment when kseg > 0), x octets per builder
+// lane (vo), and the segment length in values (kseg, 0 for a single
+// segment), for a device of `cus` compute units.  launch_cols_mfma launches
+// on the stream and returns the hipError_t of the launch, or -1 without
+// launching where the plan is empty.
 struct MfmaPlan {
-    int rt, sw, vo;
+    int rt, sw, vo, kseg;
 };
 MfmaPlan cols_mfma_plan(int wfmt, int ncols, int64_t N, int64_t K, int64_t cus);
 int launch_cols_mfma(int wfmt, int ncols, const ColsArgs &c, void *stream);

@@ -436,6 +436,301 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
     }
 }
 
+// Rows longer than one LDS load of pieces: K in segments of KSEG values,
+// the pieces of two segments double-buffered in LDS, and one workgroup
+// barrier per segment.  Each segment carries its own per-column exponent
+// (its largest |x|), so a builder needs only the segment's values, which
+// it prefetches one segment ahead; W waves fold each segment's sums into
+// their running totals with that exponent.  In segment s, W wave q takes
+// steps q * SWS .. q * SWS + SWS - 1 of the segment's KSEG / 32, and keeps
+// the W of two segments in flight.
+template <int NC> __host__ __device__ constexpr int64_t seg_buf_bytes(int64_t kseg)
+{
+    return 2 * NC * piece_row_slots(kseg) * 16;
+}
+
+template <int FMT, int NC, int SWS>
+__global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_seg_kernel(const unsigned char *W, const float *x,
+                                                                         int N, int K, int RT, int KSEG, int act,
+                                                                         const float *mop, const float *rop,
+                                                                         float *dst)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int PC = 2 * NC;
+    constexpr int WPC = kMW / NC;
+    constexpr bool kBlock = Fmt<FMT>::kBlock;
+    constexpr int SPU = steps_per_unit<FMT>();
+    constexpr int SU = SWS / SPU;              // W load units per lane per segment
+    constexpr int SSU = kBlock ? SWS / 8 : 1;  // scale units per lane per segment
+    constexpr int VO = 4;                      // x octets per builder lane per segment (KSEG <= 2048)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const bool wwave = w < kMW;
+    const int n = lane & 15, g = lane >> 4;
+    const int t = w % RT, q = (w % kMW) / RT;
+    const int nseg = K / KSEG, ss = KSEG / 32;
+    const int row0 = (blockIdx.x * RT + t) * 16;
+    const int row = min(row0 + n, N - 1);
+    const int rs = (int)piece_row_slots(KSEG);
+    const int64_t bufb = seg_buf_bytes<NC>(KSEG);
+    float *smax = reinterpret_cast<float *>(lds + 2 * bufb); // [2][NC]
+
+    // builders: segment s of column c in registers (VO octets per lane,
+    // clamped), rotated per workgroup
+    const int c = (w - kMW) % NC, h = (w - kMW) / NC;
+    const bool builder = !wwave && h < WPC;
+    const int nocts = KSEG / 8;
+    const int rot = (int)(((int64_t)blockIdx.x * kWave) % nocts);
+    float xa[VO][8], xb[VO][8];
+    auto load_x = [&](float (&xv)[VO][8], int sg) {
+#pragma unroll
+        for (int i = 0; i < VO; ++i) {
+            const int o = (min(lane + kWave * i, nocts - 1) + rot) % nocts;
+            const float *xp = x + (int64_t)c * K + (int64_t)sg * KSEG + 8 * o;
+            const f32x4u a = *reinterpret_cast<const f32x4u *>(xp);
+            const f32x4u b = *reinterpret_cast<const f32x4u *>(xp + 4);
+            xv[i][0] = a.x, xv[i][1] = a.y, xv[i][2] = a.z, xv[i][3] = a.w;
+            xv[i][4] = b.x, xv[i][5] = b.y, xv[i][6] = b.z, xv[i][7] = b.w;
+        }
+    };
+    auto build = [&](const float (&xv)[VO][8], int pb) {
+        unsigned char *base = lds + pb * bufb;
+        int sh = 0;
+        if constexpr (FMT != GEMV_W_BF16) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int i = 0; i < VO; ++i) {
+                const bool ok = lane + kWave * i < nocts;
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    mx = fmaxf(mx, ok ? fabsf(xv[i][p]) : 0.0f);
+            }
+            mx = wave_max(mx);
+            int ec;
+            (void)frexpf(mx, &ec);
+            sh = kXShift - ec;
+            if (lane == 0 && h == 0)
+                smax[pb * NC + c] = mx;
+        }
+        const int opw = (nocts + WPC - 1) / WPC;
+        const int oa = h * opw, ob = min(oa + opw, nocts);
+#pragma unroll
+        for (int i = 0; i < VO; ++i) {
+            const int o = (lane + kWave * i + rot) % nocts;
+            if (lane + kWave * i < nocts && o >= oa && o < ob) {
+                unsigned hw[4], lw[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    if constexpr (FMT == GEMV_W_BF16) {
+                        const unsigned b0 = __builtin_bit_cast(unsigned, xv[i][e]);
+                        const unsigned b1 = __builtin_bit_cast(unsigned, xv[i][e + 1]);
+                        const float r0 = xv[i][e] - __builtin_bit_cast(float, b0 & 0xFFFF0000u);
+                        const float r1 = xv[i][e + 1] - __builtin_bit_cast(float, b1 & 0xFFFF0000u);
+                        hw[e / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+                        lw[e / 2] = __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, r1),
+                                                          __builtin_bit_cast(unsigned, r0), 0x07060302u);
+                    } else {
+                        const float v0 = xv[i][slot_pos<FMT>(e)], v1 = xv[i][slot_pos<FMT>(e + 1)];
+                        const f16x2 hp =
+                            __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ldexpf(v0, sh), ldexpf(v1, sh)));
+                        const float r0 = fmaf((float)hp.x, -1024.0f, ldexpf(v0, sh + kLoShift));
+                        const float r1 = fmaf((float)hp.y, -1024.0f, ldexpf(v1, sh + kLoShift));
+                        hw[e / 2] = __builtin_bit_cast(unsigned, hp);
+                        lw[e / 2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+                    }
+                }
+                u32x4 *slot = reinterpret_cast<u32x4 *>(base) + 2 * c * rs + o;
+                slot[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                slot[rs] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+            }
+        }
+    };
+
+    // W waves: W of segment s, this wave's SWS steps
+    const unsigned char *wp = W + (int64_t)row * row_bytes<FMT>(K) + 16 * g;
+    const unsigned char *sp = W + scale_plane_offset<FMT>(N, K) + (int64_t)row * (K / 32) * 2;
+    u32x4 wa[SU], wb[SU], sa[SSU], sb[SSU];
+    auto issue = [&](u32x4 (&wq)[SU], u32x4 (&sq)[SSU], int sg) {
+        const int sbase = sg * ss + q * SWS;
+        if constexpr (kBlock) {
+#pragma unroll
+            for (int v = 0; v < SSU; ++v)
+                sq[v] = *reinterpret_cast<const u32x4u *>(sp + 2 * (sbase + 8 * v));
+        }
+#pragma unroll
+        for (int u = 0; u < SU; ++u)
+            wq[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(wp + (int64_t)step_bytes<FMT>() * (sbase + SPU * u)));
+    };
+    float tot[2] = {0.0f, 0.0f};
+    auto consume = [&](const u32x4 (&wq)[SU], const u32x4 (&sq)[SSU], int pb) {
+        const u32x4 *pa = reinterpret_cast<const u32x4 *>(lds + pb * bufb) + (n % PC) * rs + g;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            if constexpr (FMT == GEMV_W_F16) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(pa[4 * (q * SWS + u)]), as_f16x8(wq[u]), acc, 0, 0, 0);
+            } else if constexpr (FMT == GEMV_W_BF16) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa[4 * (q * SWS + u)]),
+                                                               __builtin_bit_cast(bf16x8, wq[u]), acc, 0, 0, 0);
+            } else {
+                unsigned d[4] = {wq[u].x, wq[u].y, wq[u].z, wq[u].w};
+                if constexpr (FMT == GEMV_W_Q4B32)
+                    transpose4(d);
+                else
+                    permute_q8(d);
+#pragma unroll
+                for (int i = 0; i < SPU; ++i) {
+                    const int j = SPU * u + i; // step within this wave's share of the segment
+                    f16x8 b;
+                    if constexpr (FMT == GEMV_W_Q4B32) {
+                        b = unpack_q4(d[i]);
+                    } else {
+                        unsigned u0, u1, u2, u3;
+                        unpack_q8(d[2 * i], u0, u1);
+                        unpack_q8(d[2 * i + 1], u2, u3);
+                        b = as_f16x8(u32x4{u0, u1, u2, u3});
+                    }
+                    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(pa[4 * (q * SWS + j)]), b, z, 0, 0, 0);
+                    const u32x4 sv = sq[j / 8];
+                    const int k2 = (j % 8) / 2;
+                    const unsigned sd = k2 == 0 ? sv.x : (k2 == 1 ? sv.y : (k2 == 2 ? sv.z : sv.w));
+                    const float scv = (j & 1) ? f16hi(sd) : f16lo(sd);
+                    acc[0] = fmaf(scv, dd[0], acc[0]);
+                    acc[1] = fmaf(scv, dd[1], acc[1]);
+                    acc[2] = fmaf(scv, dd[2], acc[2]);
+                    acc[3] = fmaf(scv, dd[3], acc[3]);
+                }
+            }
+        }
+        // fold the segment into the totals of this lane's two columns
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if constexpr (FMT == GEMV_W_BF16) {
+                tot[u] += acc[2 * u] + acc[2 * u + 1];
+            } else {
+                int eb;
+                (void)frexpf(smax[pb * NC + min(2 * g + u, NC - 1)], &eb);
+                tot[u] += ldexpf(fmaf(acc[2 * u + 1], 1.0f / 1024.0f, acc[2 * u]), eb - kXShift);
+            }
+        }
+    };
+
+    // The two roles run separate loops with the same sequence of barriers
+    // (so that each role's registers are live only in its own loop): x of
+    // segments 0 and 1 is queued before any W load; then one barrier per
+    // segment: segment s's pieces are ready, and segment s - 1's buffer is free.
+    if (wwave) {
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const float *opnd = (act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL) ? mop : (act == GEMV_ACT_ADD ? rop : nullptr);
+        float ov[2] = {0.0f, 0.0f};
+        if (opnd != nullptr && q == 0) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                ov[u] = opnd[(int64_t)min(2 * g + u, NC - 1) * N + row];
+        }
+        issue(wa, sa, 0);
+        if (nseg > 1)
+            issue(wb, sb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        // segment s: consume it, then issue segment s + 2 into its registers
+        for (int sg = 0; sg < nseg; sg += 2) {
+            consume(wa, sa, 0);
+            if (sg + 2 < nseg)
+                issue(wa, sa, sg + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            if (sg + 1 < nseg) {
+                consume(wb, sb, 1);
+                if (sg + 3 < nseg)
+                    issue(wb, sb, sg + 3);
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier();
+            }
+        }
+        // the slices' totals meet in LDS
+        float2 *red = reinterpret_cast<float2 *>(lds);
+        red[w * kWave + lane] = float2{tot[0], tot[1]};
+        lds_barrier();
+        if (q == 0) {
+            const int KS = kMW / RT;
+            float2 sum = red[t * kWave + lane];
+            for (int qq = 1; qq < KS; ++qq) {
+                const float2 v = red[(t + qq * RT) * kWave + lane];
+                sum.x += v.x;
+                sum.y += v.y;
+            }
+            const int ro = row0 + n;
+            if (ro < N) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int b = 2 * g + u;
+                    if (b < NC)
+                        dst[(int64_t)b * N + ro] = apply_epilogue(act, u ? sum.y : sum.x, ov[u]);
+                }
+            }
+        }
+    } else {
+        if (builder) {
+            load_x(xa, 0);
+            if (nseg > 1)
+                load_x(xb, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        if (builder)
+            build(xa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        // during segment s: prefetch x of s + 2, build the pieces of s + 1
+        for (int sg = 0; sg < nseg; sg += 2) {
+            if (builder) {
+                if (sg + 2 < nseg)
+                    load_x(xa, sg + 2);
+                if (sg + 1 < nseg)
+                    build(xb, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            if (sg + 1 < nseg) {
+                if (builder) {
+                    if (sg + 3 < nseg)
+                        load_x(xb, sg + 3);
+                    if (sg + 2 < nseg)
+                        build(xa, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier();
+            }
+        }
+        lds_barrier(); // the slices' totals are written
+    }
+}
+
+template <int FMT, int NC, int SWS> int launch_mfma_seg(const ColsArgs &c, int RT, int kseg, hipStream_t s)
+{
+    const void *fn = reinterpret_cast<const void *>(&gemv_cols_mfma_seg_kernel<FMT, NC, SWS>);
+    const int64_t lds = 2 * seg_buf_bytes<NC>(kseg) + 2 * NC * 4;
+    if (lds > 64 * 1024) {
+        static std::once_flag once;
+        static hipError_t attr_err = hipSuccess;
+        std::call_once(once, [&] { attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds); });
+        if (attr_err != hipSuccess)
+            return (int)attr_err;
+    }
+    const int grid = (c.N + 16 * RT - 1) / (16 * RT);
+    const unsigned char *W = c.W;
+    const float *x = c.x;
+    int N = c.N, K = c.K, rt = RT, ks = kseg, act = c.act;
+    const float *m = c.m, *r = c.r;
+    float *dst = c.dst;
+    void *args[] = {&W, &x, &N, &K, &rt, &ks, &act, &m, &r, &dst};
+    return (int)hipLaunchKernel(fn, dim3(grid), dim3(kWG * kWave), args, (size_t)lds, s);
+}
+
 template <int FMT, int NC, int SW, int VO> int launch_mfma(const ColsArgs &c, int RT, hipStream_t s)
 {
     const void *fn = reinterpret_cast<const void *>(&gemv_cols_mfma_kernel<FMT, NC, SW, VO>);
@@ -462,7 +757,8 @@ template <int FMT, int NC, int SW, int VO> int launch_mfma(const ColsArgs &c, in
 // per workgroup, then the unpack after the pieces are ready) is about 4-6 us
 // over the weight stream, while the vector-ALU kernel's time grows with
 // every column once the multiply-adds outrun the stream.  f16/bf16: from
-// five columns where K >= 4096, from seven on shorter rows.  8-bit: from
+// five columns where 4096 <= K <= 6144 (one segment), from seven on
+// shorter or segmented rows.  8-bit: from
 // four where the matrix is 20 MB or more and the tiles make one round of
 // workgroups, from six on 32 MB or more.  4-bit: from three on 16 MB or
 // more, from six on smaller matrices.
@@ -470,7 +766,7 @@ bool mfma_wins(int wfmt, int NC, int64_t K, int64_t tiles, int64_t cus, int64_t 
 {
     const int64_t MB = 1 << 20;
     if (wfmt == GEMV_W_F16 || wfmt == GEMV_W_BF16)
-        return NC >= (K >= 4096 ? 5 : 7);
+        return NC >= (K >= 4096 && K <= 6144 ? 5 : 7);
     if (wfmt == GEMV_W_Q8B32)
         return (NC >= 4 && wbytes >= 20 * MB && tiles <= cus) || (NC >= 6 && wbytes >= 32 * MB);
     return NC >= (wbytes >= 16 * MB ? 3 : 6);
@@ -492,6 +788,8 @@ template <int FMT, int NC, int SW> int launch_mfma_vo(const ColsArgs &c, const M
 
 template <int FMT, int NC> int launch_mfma_plan(const ColsArgs &c, const MfmaPlan &p, hipStream_t s)
 {
+    if (p.kseg)
+        return launch_mfma_seg<FMT, NC, 8>(c, p.rt, p.kseg, s);
     constexpr int SW1 = Fmt<FMT>::kBlock ? 32 : 16;
     if constexpr (FMT == GEMV_W_Q4B32) {
         if (p.sw > SW1)
@@ -525,35 +823,45 @@ template <int NC> int launch_mfma_fmt(int wfmt, const ColsArgs &c, const MfmaPla
 // the pieces within LDS.
 MfmaPlan cols_mfma_plan(int wfmt, int ncols, int64_t N, int64_t K, int64_t cus)
 {
-    MfmaPlan p{0, 0, 0};
+    MfmaPlan p{0, 0, 0, 0};
     if (wfmt == GEMV_W_F32 || wfmt < 0 || wfmt > GEMV_W_Q4B32 || ncols < 2 || ncols > 8 || N < 1)
         return p;
     const bool block = wfmt == GEMV_W_Q8B32 || wfmt == GEMV_W_Q4B32;
-    if (K < 1 || K % (block ? 256 : 32) != 0 || K > kWave * 8 * 12)
-        return p;
-    if (mfma_union_bytes(2 * ncols * piece_row_slots(K) * 16) + kMW * 4 > kMaxLds)
+    if (K < 1 || K % (block ? 256 : 32) != 0 || K >= GEMV_MAX_DIM_EXTENT)
         return p;
     const int64_t tiles = (N + 15) / 16;
     if (!mfma_wins(wfmt, ncols, K, tiles, cus, N * row_bytes_of(wfmt, K)))
         return p;
-    const int sw1 = block ? 32 : 16;
-    const int swmax = wfmt == GEMV_W_Q4B32 ? 64 : sw1;
-    int rt = 1;
-    while (rt < kMW && tiles > cus * rt)
-        rt *= 2;
-    for (; rt >= 1; rt /= 2) {
-        const int spw = mfma_spw((int)(K / 32), kMW / rt, block);
-        if (!block && tiles > cus)
-            break;
-        if (spw <= swmax) {
-            p.rt = rt;
-            p.sw = spw <= sw1 ? sw1 : swmax;
-            break;
+    int rt1 = 1; // tiles per workgroup for one round of workgroups
+    while (rt1 < kMW && tiles > cus * rt1)
+        rt1 *= 2;
+    // the whole row as one segment
+    if (K <= kWave * 8 * 12 && mfma_union_bytes(2 * ncols * piece_row_slots(K) * 16) + kMW * 4 <= kMaxLds) {
+        const int sw1 = block ? 32 : 16;
+        const int swmax = wfmt == GEMV_W_Q4B32 ? 64 : sw1;
+        for (int rt = rt1; rt >= 1; rt /= 2) {
+            const int spw = mfma_spw((int)(K / 32), kMW / rt, block);
+            if (!block && tiles > cus)
+                break;
+            if (spw <= swmax) {
+                const int64_t vo = (K / 8 + kWave - 1) / kWave; // x octets per builder lane
+                p = MfmaPlan{rt, spw <= sw1 ? sw1 : swmax, vo <= 4 ? 4 : (vo <= 8 ? 8 : 12), 0};
+                return p;
+            }
         }
+        return p;
     }
-    if (p.rt) {
-        const int64_t vo = (K / 8 + kWave - 1) / kWave; // x octets per builder lane
-        p.vo = vo <= 4 ? 4 : (vo <= 8 ? 8 : 12);
+    // segments of kseg = 2048 / rt values, so that every W wave takes 8 steps
+    // of each segment (more would not fit its registers beside the second
+    // segment in flight); kseg must divide K and two piece buffers fit LDS
+    for (int rt = rt1; rt >= 1; rt /= 2) {
+        const int kseg = 2048 / rt;
+        if (!block && tiles > cus * rt)
+            continue;
+        if (K % kseg != 0 || 2 * (2 * ncols * piece_row_slots(kseg) * 16) + 2 * ncols * 4 > kMaxLds)
+            continue;
+        p = MfmaPlan{rt, 8, 4, kseg};
+        return p;
     }
     return p;
 }

@@ -137,7 +137,8 @@ def test_ncols_inplace_and_view():
 
 @pytest.mark.parametrize("fmt,N,K,act", [("q4b32", 14336, 4096, "silu"), ("bf16", 14336, 4096, "silu_mul"),
                                          ("f16", 4096, 4096, "add"), ("q4b32", 4096, 14336, "add"),
-                                         ("q8b32", 14336, 4096, "mul")])
+                                         ("q8b32", 14336, 4096, "mul"), ("q8b32", 4096, 6144, "silu"),
+                                         ("bf16", 4096, 14336, "add")])
 def test_ncols_full_size(fmt, N, K, act):
     rng = np.random.default_rng(8)
     w = synth.random_weights(rng, fmt, N, K)
@@ -231,9 +232,10 @@ def test_ncols_wide_range_columns(fmt, N, K):
     ("f16", 4096, 4096, 4, "columns"), ("f16", 14336, 4096, 8, "columns"),
     ("q4b32", 14336, 4096, 4, "columns_matrix"), ("q4b32", 14336, 4096, 8, "columns_matrix"),
     ("q4b32", 300, 4096, 8, "columns_matrix"), ("q4b32", 4100, 2048, 7, "columns_matrix"),
-    ("q4b32", 4096, 4096, 2, "columns"), ("q4b32", 4096, 14336, 8, "columns"), ("q4b32", 33, 96, 8, "columns"),
+    ("q4b32", 4096, 4096, 2, "columns"), ("q4b32", 4096, 14336, 8, "columns_matrix"), ("q4b32", 33, 96, 8, "columns"),
+    ("q4b32", 67, 14336, 6, "columns_matrix"), ("f16", 4096, 14336, 8, "columns_matrix"), ("f16", 4096, 14336, 6, "columns"),
     ("q8b32", 4096, 6144, 4, "columns_matrix"), ("q8b32", 14336, 4096, 8, "columns_matrix"),
-    ("q8b32", 4096, 6144, 8, "columns"), ("q8b32", 4096, 4096, 4, "columns"),
+    ("q8b32", 4096, 6144, 8, "columns_matrix"), ("q8b32", 4096, 4096, 4, "columns"), ("q8b32", 4096, 14336, 3, "columns"),
     ("bf16", 4096, 4096, 8, "columns_matrix"), ("bf16", 4096, 4096, 4, "columns"), ("bf16", 14336, 4096, 8, "columns"),
     ("bf16", 4096, 2048, 6, "columns"), ("bf16", 4096, 2048, 8, "columns_matrix"),
     ("f32", 4096, 4096, 8, "columns"), ("f32", 64, 1001, 4, "columns_generic"), ("f16", 64, 64, 1, "one_column")])
