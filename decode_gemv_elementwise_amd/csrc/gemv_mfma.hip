@@ -57,7 +57,6 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4))); // x may be 4-byte aligned only
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4u __attribute__((ext_vector_type(4), aligned(4))); // scale runs: 4-byte aligned
 
 constexpr int kMW = 8;      // W and matrix-core waves per workgroup
