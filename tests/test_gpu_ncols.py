@@ -242,3 +242,34 @@ def test_ncols_wide_range_columns(fmt, N, K):
 def test_ncols_kernel_choice(fmt, N, K, ncols, kernel):
     """The shapes the tests above rely on to reach each kernel take it."""
     assert binding.gemv_ncols_kernel(fmt, N, K, ncols) == kernel
+
+
+MATRIX_SHAPES = [("f16", 300, 4096, 8), ("bf16", 300, 4096, 6), ("q4b32", 300, 4096, 7), ("q8b32", 4096, 6144, 4),
+                 ("q4b32", 67, 14336, 8), ("f16", 67, 14336, 7), ("q8b32", 4096, 6144, 8)]
+
+
+@pytest.mark.parametrize("fmt,N,K,B", MATRIX_SHAPES)
+@pytest.mark.parametrize("act", ALL_ACTS)
+def test_ncols_matrix_core_epilogues(fmt, N, K, B, act):
+    """Every epilogue on the matrix-core kernels (single segment and
+    segmented, as the kernel query confirms)."""
+    assert binding.gemv_ncols_kernel(fmt, N, K, B) == "columns_matrix"
+    rng = np.random.default_rng(zlib.crc32(f"mx/{fmt}/{N}/{K}/{act}".encode()))
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(B, K)).astype(np.float32)
+    M, R = _operands(rng, act, B, N)
+    check_ncols(w, X, act, M, R, tag=f"matrix {act}")
+
+
+@pytest.mark.parametrize("fmt,N,K,B", [("q4b32", 14336 + 37, 4096, 4), ("q4b32", 8192 + 5, 2048, 6),
+                                       ("q8b32", 14336 + 21, 4096, 6), ("q4b32", 4096 + 3, 14336, 3),
+                                       ("f16", 4096 - 9, 4096, 6)])
+def test_ncols_matrix_core_ragged_rows(fmt, N, K, B):
+    """Row counts that leave the last 16-row tile (and the last workgroup of
+    2 or 4 tiles) partly empty."""
+    assert binding.gemv_ncols_kernel(fmt, N, K, B) == "columns_matrix"
+    rng = np.random.default_rng(N + K + B)
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(B, K)).astype(np.float32)
+    R = rng.normal(size=(B, N)).astype(np.float32)
+    check_ncols(w, X, "add", R=R, tag="ragged")
