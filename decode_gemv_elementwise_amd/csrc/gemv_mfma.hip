@@ -196,6 +196,78 @@ __host__ __device__ inline int mfma_spw(int nsteps, int KS, bool block)
     return block ? (spw + 7) & ~7 : spw;
 }
 
+// The hi and lo pieces of one octet of x (v, in position order) into their
+// A-layout slots: slot[0] (hi) and slot[rs] (lo).  sh: the column's scale
+// exponent (unused for bf16, whose pieces are not scaled).
+template <int FMT> __device__ __forceinline__ void write_pieces(const float (&v)[8], int sh, u32x4 *slot, int rs)
+{
+    unsigned hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        if constexpr (FMT == GEMV_W_BF16) {
+            const unsigned b0 = __builtin_bit_cast(unsigned, v[e]), b1 = __builtin_bit_cast(unsigned, v[e + 1]);
+            const float r0 = v[e] - __builtin_bit_cast(float, b0 & 0xFFFF0000u);
+            const float r1 = v[e + 1] - __builtin_bit_cast(float, b1 & 0xFFFF0000u);
+            hw[e / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+            lw[e / 2] = __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, r1), __builtin_bit_cast(unsigned, r0), 0x07060302u);
+        } else {
+            const float v0 = v[slot_pos<FMT>(e)], v1 = v[slot_pos<FMT>(e + 1)];
+            const f16x2 hp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ldexpf(v0, sh), ldexpf(v1, sh)));
+            const float r0 = fmaf((float)hp.x, -1024.0f, ldexpf(v0, sh + kLoShift));
+            const float r1 = fmaf((float)hp.y, -1024.0f, ldexpf(v1, sh + kLoShift));
+            hw[e / 2] = __builtin_bit_cast(unsigned, hp);
+            lw[e / 2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+        }
+    }
+    slot[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    slot[rs] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+}
+
+// The matrix-core steps of one W load unit (SPU steps): pa[4 * s] is the A
+// operand of step s; j is the unit's first step within the wave's slice,
+// whose block scales sq[j / 8] holds.  16-bit weights accumulate in the
+// matrix core; block formats scale each step's sums into acc.
+template <int FMT>
+__device__ __forceinline__ void mfma_unit(f32x4 &acc, const u32x4 &w, const u32x4 *pa, int s, int j, const u32x4 *sq)
+{
+    if constexpr (FMT == GEMV_W_F16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(pa[4 * s]), as_f16x8(w), acc, 0, 0, 0);
+    } else if constexpr (FMT == GEMV_W_BF16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa[4 * s]), __builtin_bit_cast(bf16x8, w),
+                                                       acc, 0, 0, 0);
+    } else {
+        constexpr int SPU = steps_per_unit<FMT>();
+        unsigned d[4] = {w.x, w.y, w.z, w.w};
+        if constexpr (FMT == GEMV_W_Q4B32)
+            transpose4(d);
+        else
+            permute_q8(d);
+#pragma unroll
+        for (int i = 0; i < SPU; ++i) {
+            f16x8 b;
+            if constexpr (FMT == GEMV_W_Q4B32) {
+                b = unpack_q4(d[i]);
+            } else {
+                unsigned u0, u1, u2, u3;
+                unpack_q8(d[2 * i], u0, u1);
+                unpack_q8(d[2 * i + 1], u2, u3);
+                b = as_f16x8(u32x4{u0, u1, u2, u3});
+            }
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(pa[4 * (s + i)]), b, z, 0, 0, 0);
+            const int jj = j + i;
+            const u32x4 sv = sq[jj / 8];
+            const int k2 = (jj % 8) / 2;
+            const unsigned sd = k2 == 0 ? sv.x : (k2 == 1 ? sv.y : (k2 == 2 ? sv.z : sv.w));
+            const float scv = (jj & 1) ? f16hi(sd) : f16lo(sd);
+            acc[0] = fmaf(scv, dd[0], acc[0]);
+            acc[1] = fmaf(scv, dd[1], acc[1]);
+            acc[2] = fmaf(scv, dd[2], acc[2]);
+            acc[3] = fmaf(scv, dd[3], acc[3]);
+        }
+    }
+}
+
 template <int FMT, int NC, int SW, int VO>
 __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsigned char *W, const float *x, int N,
                                                                      int K, int RT, int act, const float *mop,
@@ -288,20 +360,8 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
 #pragma unroll
         for (int i = 0; i < VO; ++i) {
             const int o = (lane + kWave * i + rot) % nocts;
-            if (lane + kWave * i < nocts && o >= oa && o < ob) {
-                unsigned hw[4], lw[4];
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const unsigned b0 = __builtin_bit_cast(unsigned, xv[i][e]), b1 = __builtin_bit_cast(unsigned, xv[i][e + 1]);
-                    const float r0 = xv[i][e] - __builtin_bit_cast(float, b0 & 0xFFFF0000u);
-                    const float r1 = xv[i][e + 1] - __builtin_bit_cast(float, b1 & 0xFFFF0000u);
-                    hw[e / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-                    lw[e / 2] = __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, r1), __builtin_bit_cast(unsigned, r0), 0x07060302u);
-                }
-                u32x4 *slot = reinterpret_cast<u32x4 *>(lds) + 2 * c * rs + o;
-                slot[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-                slot[rs] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-            }
+            if (lane + kWave * i < nocts && o >= oa && o < ob)
+                write_pieces<FMT>(xv[i], 0, reinterpret_cast<u32x4 *>(lds) + 2 * c * rs + o, rs);
         }
     } else if (h < WPC) {
         // builders: column maximum -> binary exponent, then hi / lo pieces
@@ -326,21 +386,8 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
 #pragma unroll
         for (int i = 0; i < VO; ++i) {
             const int o = (lane + kWave * i + rot) % nocts;
-            if (lane + kWave * i < nocts && o >= oa && o < ob) {
-                unsigned hw[4], lw[4];
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float v0 = xv[i][slot_pos<FMT>(e)], v1 = xv[i][slot_pos<FMT>(e + 1)];
-                    const f16x2 hp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ldexpf(v0, sh), ldexpf(v1, sh)));
-                    const float r0 = fmaf((float)hp.x, -1024.0f, ldexpf(v0, sh + kLoShift));
-                    const float r1 = fmaf((float)hp.y, -1024.0f, ldexpf(v1, sh + kLoShift));
-                    hw[e / 2] = __builtin_bit_cast(unsigned, hp);
-                    lw[e / 2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-                }
-                u32x4 *slot = reinterpret_cast<u32x4 *>(lds) + 2 * c * rs + o;
-                slot[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-                slot[rs] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-            }
+            if (lane + kWave * i < nocts && o >= oa && o < ob)
+                write_pieces<FMT>(xv[i], sh, reinterpret_cast<u32x4 *>(lds) + 2 * c * rs + o, rs);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -357,45 +404,8 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
                 wq[u + PU] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp + (int64_t)step_bytes<FMT>() * s));
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (SPU * u < cnt) {
-                if constexpr (FMT == GEMV_W_F16) {
-                    const f16x8 a = as_f16x8(pa[4 * (s0 + u)]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_f16x8(wq[u]), acc, 0, 0, 0);
-                } else if constexpr (FMT == GEMV_W_BF16) {
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, pa[4 * (s0 + u)]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, wq[u]), acc, 0, 0, 0);
-                } else {
-                    unsigned d[4] = {wq[u].x, wq[u].y, wq[u].z, wq[u].w};
-                    if constexpr (FMT == GEMV_W_Q4B32)
-                        transpose4(d);
-                    else
-                        permute_q8(d);
-#pragma unroll
-                    for (int i = 0; i < SPU; ++i) {
-                        const int j = SPU * u + i; // step within the slice
-                        f16x8 b;
-                        if constexpr (FMT == GEMV_W_Q4B32) {
-                            b = unpack_q4(d[i]);
-                        } else {
-                            unsigned u0, u1, u2, u3;
-                            unpack_q8(d[2 * i], u0, u1);
-                            unpack_q8(d[2 * i + 1], u2, u3);
-                            b = as_f16x8(u32x4{u0, u1, u2, u3});
-                        }
-                        const f16x8 a = as_f16x8(pa[4 * (s0 + j)]);
-                        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-                        const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, z, 0, 0, 0);
-                        const u32x4 sv = sq[j / 8];
-                        const int k2 = (j % 8) / 2;
-                        const unsigned sd = k2 == 0 ? sv.x : (k2 == 1 ? sv.y : (k2 == 2 ? sv.z : sv.w));
-                        const float scv = (j & 1) ? f16hi(sd) : f16lo(sd);
-                        acc[0] = fmaf(scv, dd[0], acc[0]);
-                        acc[1] = fmaf(scv, dd[1], acc[1]);
-                        acc[2] = fmaf(scv, dd[2], acc[2]);
-                        acc[3] = fmaf(scv, dd[3], acc[3]);
-                    }
-                }
-            }
+            if (SPU * u < cnt)
+                mfma_unit<FMT>(acc, wq[u], pa, s0 + SPU * u, SPU * u, sq);
         }
     }
 
@@ -493,7 +503,6 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_seg_kernel(const un
         }
     };
     auto build = [&](const float (&xv)[VO][8], int pb) {
-        unsigned char *base = lds + pb * bufb;
         int sh = 0;
         if constexpr (FMT != GEMV_W_BF16) {
             float mx = 0.0f;
@@ -516,32 +525,8 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_seg_kernel(const un
 #pragma unroll
         for (int i = 0; i < VO; ++i) {
             const int o = (lane + kWave * i + rot) % nocts;
-            if (lane + kWave * i < nocts && o >= oa && o < ob) {
-                unsigned hw[4], lw[4];
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    if constexpr (FMT == GEMV_W_BF16) {
-                        const unsigned b0 = __builtin_bit_cast(unsigned, xv[i][e]);
-                        const unsigned b1 = __builtin_bit_cast(unsigned, xv[i][e + 1]);
-                        const float r0 = xv[i][e] - __builtin_bit_cast(float, b0 & 0xFFFF0000u);
-                        const float r1 = xv[i][e + 1] - __builtin_bit_cast(float, b1 & 0xFFFF0000u);
-                        hw[e / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-                        lw[e / 2] = __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, r1),
-                                                          __builtin_bit_cast(unsigned, r0), 0x07060302u);
-                    } else {
-                        const float v0 = xv[i][slot_pos<FMT>(e)], v1 = xv[i][slot_pos<FMT>(e + 1)];
-                        const f16x2 hp =
-                            __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ldexpf(v0, sh), ldexpf(v1, sh)));
-                        const float r0 = fmaf((float)hp.x, -1024.0f, ldexpf(v0, sh + kLoShift));
-                        const float r1 = fmaf((float)hp.y, -1024.0f, ldexpf(v1, sh + kLoShift));
-                        hw[e / 2] = __builtin_bit_cast(unsigned, hp);
-                        lw[e / 2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-                    }
-                }
-                u32x4 *slot = reinterpret_cast<u32x4 *>(base) + 2 * c * rs + o;
-                slot[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-                slot[rs] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-            }
+            if (lane + kWave * i < nocts && o >= oa && o < ob)
+                write_pieces<FMT>(xv[i], sh, reinterpret_cast<u32x4 *>(lds + pb * bufb) + 2 * c * rs + o, rs);
         }
     };
 
@@ -566,43 +551,8 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_seg_kernel(const un
         const u32x4 *pa = reinterpret_cast<const u32x4 *>(lds + pb * bufb) + (n % PC) * rs + g;
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int u = 0; u < SU; ++u) {
-            if constexpr (FMT == GEMV_W_F16) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(pa[4 * (q * SWS + u)]), as_f16x8(wq[u]), acc, 0, 0, 0);
-            } else if constexpr (FMT == GEMV_W_BF16) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa[4 * (q * SWS + u)]),
-                                                               __builtin_bit_cast(bf16x8, wq[u]), acc, 0, 0, 0);
-            } else {
-                unsigned d[4] = {wq[u].x, wq[u].y, wq[u].z, wq[u].w};
-                if constexpr (FMT == GEMV_W_Q4B32)
-                    transpose4(d);
-                else
-                    permute_q8(d);
-#pragma unroll
-                for (int i = 0; i < SPU; ++i) {
-                    const int j = SPU * u + i; // step within this wave's share of the segment
-                    f16x8 b;
-                    if constexpr (FMT == GEMV_W_Q4B32) {
-                        b = unpack_q4(d[i]);
-                    } else {
-                        unsigned u0, u1, u2, u3;
-                        unpack_q8(d[2 * i], u0, u1);
-                        unpack_q8(d[2 * i + 1], u2, u3);
-                        b = as_f16x8(u32x4{u0, u1, u2, u3});
-                    }
-                    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(pa[4 * (q * SWS + j)]), b, z, 0, 0, 0);
-                    const u32x4 sv = sq[j / 8];
-                    const int k2 = (j % 8) / 2;
-                    const unsigned sd = k2 == 0 ? sv.x : (k2 == 1 ? sv.y : (k2 == 2 ? sv.z : sv.w));
-                    const float scv = (j & 1) ? f16hi(sd) : f16lo(sd);
-                    acc[0] = fmaf(scv, dd[0], acc[0]);
-                    acc[1] = fmaf(scv, dd[1], acc[1]);
-                    acc[2] = fmaf(scv, dd[2], acc[2]);
-                    acc[3] = fmaf(scv, dd[3], acc[3]);
-                }
-            }
-        }
+        for (int u = 0; u < SU; ++u)
+            mfma_unit<FMT>(acc, wq[u], pa, q * SWS + SPU * u, SPU * u, sq);
         // fold the segment into the totals of this lane's two columns
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
