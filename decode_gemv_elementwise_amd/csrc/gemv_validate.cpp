@@ -15,6 +15,7 @@
 // add: f32, identically shaped (no broadcast), row-contiguous.
 #include "gemv_internal.h"
 
+#include <climits>
 #include <cstdint>
 
 namespace gemv {
@@ -27,6 +28,9 @@ int64_t weight_bytes(int wfmt, int64_t N, int64_t K)
         return GEMV_E_DIM;
     switch (wfmt) {
     case GEMV_W_F32:
+        // N * K < 2^62 cannot overflow; four bytes per weight can
+        if (N * K > INT64_MAX / 4)
+            return GEMV_E_DIM;
         return N * K * 4;
     case GEMV_W_F16:
     case GEMV_W_BF16:
@@ -86,10 +90,16 @@ bool same_shape(const gemv_view *a, const gemv_view *b)
     return true;
 }
 
+// [p, p + bytes) as addresses.  A span that would run past the top of the
+// address space is no real buffer: it is widened to the whole space, so that
+// it overlaps every other buffer and the call is rejected.
 Span span_of(const void *p, int64_t bytes)
 {
-    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    return Span{lo, lo + static_cast<uintptr_t>(bytes)};
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    const uintptr_t b = static_cast<uintptr_t>(bytes);
+    if (b > UINTPTR_MAX - lo)
+        return Span{0, UINTPTR_MAX};
+    return Span{lo, lo + b};
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -219,7 +229,8 @@ int validate_fwht(const float *x, const float *signs, int64_t nrows, int64_t K, 
 {
     if (!x || !signs || !dst)
         return GEMV_E_NULL;
-    if (nrows < 1 || K < 1 || K >= GEMV_MAX_DIM_EXTENT || nrows * K >= GEMV_MAX_DIM_EXTENT)
+    if (nrows < 1 || K < 1 || nrows >= GEMV_MAX_DIM_EXTENT || K >= GEMV_MAX_DIM_EXTENT ||
+        nrows * K >= GEMV_MAX_DIM_EXTENT)
         return GEMV_E_DIM;
     int st = check_fwht_shape(K, n, nsigns);
     if (st != GEMV_OK)

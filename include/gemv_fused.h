@@ -93,9 +93,10 @@ typedef enum {
 enum {
     GEMV_OK = 0,
     GEMV_E_NULL = -1,    /* a required pointer (W, x, acc, dst, a view's data) is NULL */
-    GEMV_E_DIM = -2,     /* N or K < 1 or too large, K % 32 != 0 for a block
-                            format, ncols outside 1..GEMV_MAX_NCOLS, or the
-                            dst view does not hold ncols * N elements */
+    GEMV_E_DIM = -2,     /* N or K < 1 or too large (also when W's byte
+                            count would not fit in int64_t), K % 32 != 0 for
+                            a block format, ncols outside 1..GEMV_MAX_NCOLS,
+                            or the dst view does not hold ncols * N elements */
     GEMV_E_FMT = -3,     /* unknown weight format */
     GEMV_E_ACT = -4,     /* unknown epilogue */
     GEMV_E_OPERAND = -5, /* the epilogue's operand is missing, or an operand it
@@ -104,7 +105,9 @@ enum {
                             is not C-contiguous, or an operand whose shape
                             differs from dst's */
     GEMV_E_ALIAS = -7,   /* dst overlaps W, x or acc/operands other than by
-                            being the identical view */
+                            being the identical view; a buffer whose bytes
+                            would run past the top of the address space
+                            counts as overlapping every other buffer */
     GEMV_E_ALIGN = -8,   /* W not 16-byte aligned, or an f32 pointer not
                             4-byte aligned */
     GEMV_E_HIP = -9      /* the HIP launch failed; see gemv_last_hip_error() */

@@ -53,6 +53,10 @@ def test_weight_bytes_errors():
     assert b.gemv_weight_bytes("f32", 0, 4) == S["GEMV_E_DIM"]
     assert b.gemv_weight_bytes(7, 4, 4) == S["GEMV_E_FMT"]
     assert b.gemv_weight_bytes("f32", 1 << 31, 4) == S["GEMV_E_DIM"]
+    # both extents legal, but four bytes per weight no longer fit in int64
+    big = (1 << 31) - 1
+    assert b.gemv_weight_bytes("f32", big, big) == S["GEMV_E_DIM"]
+    assert b.gemv_weight_bytes("f16", big, big) == 2 * big * big
 
 
 def v(addr, shape, stride=None):
@@ -156,6 +160,14 @@ def test_alias_rules():
     assert val(act="mul", mul_operand=v(M0, (64,)), dst=v(M0 + 252, (64,))) == S["GEMV_E_ALIAS"]
     # the check is stateless: a refused call does not change the next verdict
     assert val(act="add", add_operand=v(R0, (64,)), dst=v(R0, (64,))) == S["GEMV_OK"]
+    # a buffer running past the top of the address space is no buffer: it
+    # counts as overlapping everything (dst lies in what a wrapped span of W
+    # would otherwise have reached from address 0)
+    top = (1 << 64) - 256
+    assert val(W=top, dst=v(256, (64,))) == S["GEMV_E_ALIAS"]
+    assert val(x=top + 128, dst=v(256, (64,))) == S["GEMV_E_ALIAS"]
+    assert val(dst=v(top + 192, (64,))) == S["GEMV_E_ALIAS"]
+    assert val(W=top - wbytes, dst=v(256, (64,))) == S["GEMV_OK"]          # ends just below the top
 
 
 def eval_(act="none", N=64, acc=X0, mul=None, add=None, dst=None):
@@ -267,6 +279,7 @@ def test_fwht_validate():
     assert fval(nsigns=1) == S["GEMV_OK"]
     assert fval(nrows=0) == S["GEMV_E_DIM"]
     assert fval(nrows=1 << 20, K=4096) == S["GEMV_E_DIM"]   # nrows * K too large
+    assert fval(nrows=(1 << 63) - 1, K=4096) == S["GEMV_E_DIM"]   # no overflow in nrows * K
     assert fval(x=0) == S["GEMV_E_NULL"] and fval(signs=0) == S["GEMV_E_NULL"] and fval(dst=0) == S["GEMV_E_NULL"]
     assert fval(x=X0 + 2) == S["GEMV_E_ALIGN"] and fval(signs=M0 + 1) == S["GEMV_E_ALIGN"]
     assert fval(dst=X0) == S["GEMV_OK"]                     # in place

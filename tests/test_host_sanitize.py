@@ -1,0 +1,39 @@
+"""The host-side argument checker under AddressSanitizer and
+UndefinedBehaviorSanitizer: tests/host/validate_fuzz.cpp is built with g++
+together with csrc/gemv_validate.cpp and drives every checking entry point
+with random, extreme and malformed arguments (see that file for the
+properties it checks).  CPU only; no HIP code is built here."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FLAGS = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+         "-fno-sanitize-recover=all"]
+
+
+def _build(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "validate_fuzz")
+    cmd = [gxx, *FLAGS, "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROOT, "decode_gemv_elementwise_amd", "csrc"),
+           os.path.join(ROOT, "tests", "host", "validate_fuzz.cpp"),
+           os.path.join(ROOT, "decode_gemv_elementwise_amd", "csrc", "gemv_validate.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    if r.returncode != 0 and "sanitize" in r.stderr and ("cannot find" in r.stderr or "not supported" in r.stderr):
+        pytest.skip("sanitizer runtime not available: " + r.stderr[-300:])
+    assert r.returncode == 0, r.stderr[-3000:]
+    return exe
+
+
+def test_checker_under_sanitizers(tmp_path):
+    exe = _build(tmp_path)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe, "300000"], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
+    assert r.stdout.startswith("ok 300000 iterations")
