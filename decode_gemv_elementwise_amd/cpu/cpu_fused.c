@@ -155,6 +155,7 @@ typedef struct {
     int act;
     const float *m, *r;
     float *dst;
+    float *acc; /* where the unfused product goes (dst itself when no scratch is given) */
     int fused;
     int64_t lo, hi; /* rows of this thread */
 } Job;
@@ -233,7 +234,7 @@ static void *run_rows(void *arg)
         if (j->fused)
             epilogue_span(j->act, nt, tile, j->m ? j->m + r0 : NULL, j->r ? j->r + r0 : NULL, j->dst + r0);
         else
-            memcpy(j->dst + r0, tile, (size_t)nt * sizeof(float));
+            memcpy(j->acc + r0, tile, (size_t)nt * sizeof(float));
     }
     return NULL;
 }
@@ -241,21 +242,26 @@ static void *run_rows(void *arg)
 static void *run_epilogue(void *arg)
 {
     const Job *j = (const Job *)arg;
-    epilogue_span(j->act, j->hi - j->lo, j->dst + j->lo, j->m ? j->m + j->lo : NULL, j->r ? j->r + j->lo : NULL,
+    epilogue_span(j->act, j->hi - j->lo, j->acc + j->lo, j->m ? j->m + j->lo : NULL, j->r ? j->r + j->lo : NULL,
                   j->dst + j->lo);
     return NULL;
 }
 
 #define MAX_THREADS 256
 
+static int overlaps(const float *a, const float *b, int64_t n) { return a && b && a < b + n && b < a + n; }
+
 /* dst = epilogue(W x) on the host, with nthreads threads over contiguous row
  * ranges.  fused != 0: the epilogue is applied to each 16-row accumulator
- * tile; fused == 0: all accumulators are written, the threads join, and the
- * epilogue runs as its own pass (split over the same threads).  All pointers
- * are host pointers; dst may be the identical array as m or r.  Returns 0, or
- * -1 for bad arguments. */
+ * tile; fused == 0: every product is first written to acc (N floats of
+ * caller scratch), the threads join, and the epilogue runs as its own pass
+ * from acc and the operand into dst (split over the same threads), as a
+ * separate element-wise op would.  Without acc the unfused products go to
+ * dst, which then must not overlap the operand.  All pointers are host
+ * pointers; dst may be the identical array as m or r.  Returns 0, or -1 for
+ * bad arguments. */
 int cpu_fused_gemv(int wfmt, int64_t N, int64_t K, const void *W, const float *x, int act, const float *m,
-                   const float *r, float *dst, int nthreads, int fused)
+                   const float *r, float *dst, int nthreads, int fused, float *acc)
 {
     if (wfmt < GEMV_W_F32 || wfmt > GEMV_W_Q4B32 || act < GEMV_ACT_NONE || act > GEMV_ACT_ADD || N < 1 || K < 1 ||
         !W || !x || !dst || nthreads < 1)
@@ -264,6 +270,14 @@ int cpu_fused_gemv(int wfmt, int64_t N, int64_t K, const void *W, const float *x
         return -1;
     if (((act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL) && !m) || (act == GEMV_ACT_ADD && !r))
         return -1;
+    const float *op = act == GEMV_ACT_ADD ? r : ((act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL) ? m : NULL);
+    if (!fused && act != GEMV_ACT_NONE) {
+        if (!acc && overlaps(dst, op, N))
+            return -1;
+        if (acc && (overlaps(acc, dst, N) || overlaps(acc, op, N)))
+            return -1;
+    }
+    float *prod = (!fused && act != GEMV_ACT_NONE && acc) ? acc : dst;
     if (nthreads > MAX_THREADS)
         nthreads = MAX_THREADS;
     if (nthreads > N)
@@ -271,7 +285,7 @@ int cpu_fused_gemv(int wfmt, int64_t N, int64_t K, const void *W, const float *x
     Job jobs[MAX_THREADS];
     pthread_t th[MAX_THREADS];
     for (int t = 0; t < nthreads; ++t) {
-        jobs[t] = (Job){wfmt, N, K, (const uint8_t *)W, x, act, m, r, dst, fused, N * t / nthreads,
+        jobs[t] = (Job){wfmt, N, K, (const uint8_t *)W, x, act, m, r, dst, prod, fused, N * t / nthreads,
                         N * (t + 1) / nthreads};
     }
     for (int t = 1; t < nthreads; ++t)

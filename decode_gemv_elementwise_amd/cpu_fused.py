@@ -30,7 +30,7 @@ def _lib():
             raise ImportError(f"{LIB_PATH} is not built (python -m decode_gemv_elementwise_amd.build)")
         lib = ctypes.CDLL(LIB_PATH)
         lib.cpu_fused_gemv.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, _fp,
-                                       ctypes.c_int, _fp, _fp, _fp, ctypes.c_int, ctypes.c_int]
+                                       ctypes.c_int, _fp, _fp, _fp, ctypes.c_int, ctypes.c_int, _fp]
         lib.cpu_fused_gemv.restype = ctypes.c_int
         lib.cpu_vexp_nonpos.argtypes = [ctypes.c_int64, _fp, _fp]
         lib.cpu_vexp_nonpos.restype = None
@@ -46,15 +46,19 @@ def _p(a):
     return None if a is None else a.ctypes.data_as(_fp)
 
 
-def gemv(fmt, N, K, w, x, act, m=None, r=None, out=None, threads=None, fused=True):
+def gemv(fmt, N, K, w, x, act, m=None, r=None, out=None, threads=None, fused=True, acc=None):
     """dst = epilogue(W x) on the host; returns dst (float32 [N]).  out may be
-    m or r itself (in place)."""
+    m or r itself (in place).  Unfused (fused=False), the product is written
+    to a separate buffer first (acc, or a fresh one) and the epilogue pass
+    reads it, as a GEMV followed by its own element-wise op would."""
     w = np.ascontiguousarray(w).view(np.uint8).reshape(-1)
     x, m, r = _f32(x), _f32(m), _f32(r)
     dst = np.empty(N, np.float32) if out is None else out
     threads = threads or len(os.sched_getaffinity(0))
+    if not fused and act != "none" and acc is None:
+        acc = np.empty(N, np.float32)
     rc = _lib().cpu_fused_gemv(FORMATS[fmt], N, K, w.ctypes.data, _p(x), ACTS[act], _p(m), _p(r), _p(dst),
-                               threads, 1 if fused else 0)
+                               threads, 1 if fused else 0, _p(acc))
     if rc != 0:
         raise ValueError(f"cpu_fused_gemv rejected {fmt} {N}x{K} act={act}")
     return dst

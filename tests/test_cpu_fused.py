@@ -106,6 +106,11 @@ def test_in_place_add_and_rejections():
     rr = r.copy()
     cpu_fused.gemv("bf16", N, K, w.data, x, "add", r=rr, out=rr)
     assert np.array_equal(rr, want)
+    # unfused in place: the product goes to its own buffer before the
+    # element-wise pass reads it and the operand
+    rr = r.copy()
+    cpu_fused.gemv("bf16", N, K, w.data, x, "add", r=rr, out=rr, fused=False)
+    assert np.array_equal(rr, want)
     with pytest.raises(ValueError):
         cpu_fused.gemv("q4b32", N, 48, np.zeros(4096, np.uint8), x[:48], "none")
     with pytest.raises(ValueError):
