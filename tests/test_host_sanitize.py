@@ -6,7 +6,10 @@
 - the CPU comparison GEMV: tests/host/cpu_fused_fuzz.c is built with gcc
   together with cpu/cpu_fused.c and runs random ragged shapes, every format
   and epilogue, fused and unfused, in place and not, over heap buffers of
-  exactly the documented sizes.
+  exactly the documented sizes;
+- the oracle's C code: tests/host/oracle_fuzz.c is built with gcc together
+  with oracle/gemv_oracle.c and calls every oracle routine over buffers of
+  exactly the sizes the oracle documents.
 See those files for the properties they check."""
 import os
 import shutil
@@ -63,3 +66,20 @@ def test_cpu_comparison_gemv_under_sanitizers(tmp_path):
     assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
     assert r.stdout.startswith("ok 400 iterations")
+
+
+def test_oracle_under_sanitizers(tmp_path):
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path / "oracle_fuzz")
+    cmd = [gcc, "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", os.path.join(ROOT, "tests", "host", "oracle_fuzz.c"),
+           os.path.join(ROOT, "oracle", "gemv_oracle.c"), "-lm", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe, "300"], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
+    assert r.stdout.startswith("ok 300 iterations")
