@@ -11,6 +11,7 @@ torch = pytest.importorskip("torch")
 import oracle
 from decode_gemv_elementwise_amd import binding, synth
 from gpu_util import check_ncols, check_parity, dev, host, log, run_fused
+from oracle.compare import TOLERANCE, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -268,6 +269,66 @@ def test_rejected_call_writes_nothing():
     torch.cuda.synchronize()
     assert torch.all(dst == 7.0)
     assert torch.all(alias == 0.0)
+
+
+def _separate_ops(w, Wd, xd, act, operand, dst):
+    """What a caller does when a guard refuses the fused call: the separate
+    ops ("vulkan: fuse the sign multiply into the Hadamard FWHT", Additional
+    information; "ggml-cpu: fuse element-wise epilogues ...", Guards).  The
+    product goes to scratch the caller owns, the operand to a contiguous
+    buffer of dst's shape, then the element-wise pass writes dst."""
+    tmp = torch.empty(w.N, dtype=torch.float32, device="cuda")
+    binding.gemv_fused(Wd, w.fmt, w.N, w.K, xd, "none", dst=tmp)
+    op = operand.expand(dst.shape).contiguous().clone()
+    kw = {"add_operand": op} if act == "add" else {"mul_operand": op}
+    binding.gemv_epilogue(act, w.N, tmp, dst=dst, **kw)
+    torch.cuda.synchronize()
+
+
+def test_guard_failure_falls_back_to_separate_ops():
+    """A call the guards refuse writes nothing; the caller's separate ops then
+    give the oracle's result, so only the speed changes, not the values."""
+    rng = np.random.default_rng(16)
+    cases = [
+        # dst one element past the residual in one buffer: a shifted overlap
+        ("f16", 4096, 4096, "add", "alias", binding.STATUS_CODE["GEMV_E_ALIAS"]),
+        # every other element of a larger buffer: not contiguous
+        ("q8b32", 4096, 6144, "mul", "strided", binding.STATUS_CODE["GEMV_E_LAYOUT"]),
+        # one multiplier broadcast over every row: stride 0
+        ("bf16", 1024, 4096, "silu_mul", "broadcast", binding.STATUS_CODE["GEMV_E_LAYOUT"]),
+    ]
+    for fmt, N, K, act, kind, status in cases:
+        log(f"guard fallback {fmt} {N}x{K} {act} {kind}")
+        w = synth.random_weights(rng, fmt, N, K)
+        x = synth.draw_vec(rng, K)
+        Wd, xd = dev(w.data), dev(x)
+        if kind == "alias":
+            buf = dev(np.concatenate([synth.draw_vec(rng, N), np.zeros(1, np.float32)]))
+            operand, dst = buf[:N], buf[1:]
+            values = host(operand).copy()
+        elif kind == "strided":
+            big = dev(synth.draw_vec(rng, 2 * N))
+            operand = big[::2]
+            dst = torch.full((N,), 7.0, dtype=torch.float32, device="cuda")
+            values = host(operand).copy()
+        else:
+            operand = dev(synth.draw_vec(rng, 1)).expand(N)
+            dst = torch.full((N,), 7.0, dtype=torch.float32, device="cuda")
+            values = np.full(N, host(operand)[0], np.float32)
+        before = host(dst).copy()
+        kw = {"add_operand": operand} if act == "add" else {"mul_operand": operand}
+        with pytest.raises(binding.GemvError) as e:
+            binding.gemv_fused(Wd, fmt, N, K, xd, act, dst=dst, **kw)
+        assert e.value.status == status, (kind, e.value.status)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(dst), before), kind
+        _separate_ops(w, Wd, xd, act, operand, dst)
+        g = host(dst).reshape(-1)
+        m = values if act != "add" else None
+        r = values if act == "add" else None
+        y, acc, absacc = oracle.reference(fmt, N, K, w.data, x, act, m=m, r=r)
+        res = compare(g, y, acc, absacc, act, m=m, r=r)
+        assert res["max_err"] <= TOLERANCE[fmt], (kind, res)
 
 
 # ------------------------------------------------------------------ the 4-bit layer chain
