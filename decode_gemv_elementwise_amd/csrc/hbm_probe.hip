@@ -32,6 +32,31 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *__restrict
         out[blockIdx.x] = red[0];
 }
 
+// One pass, no loop: wave w reads the 8 KiB at [8 KiB w, 8 KiB (w+1)) of the
+// buffer, lane l the 16-byte pieces l, l + 64, ..., l + 448 of it, all issued
+// before any is used (indices past the end are clamped to the last piece).
+// The sum is stored only if it equals a value it never takes, which keeps
+// the loads without writing anything.
+constexpr int kOnceLoads = 8;
+__global__ __launch_bounds__(256) void read_once_kernel(const u32x4 *__restrict__ a, int64_t n16, float *out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t base = wave * 64 * kOnceLoads;
+    u32x4 v[kOnceLoads];
+#pragma unroll
+    for (int u = 0; u < kOnceLoads; ++u) {
+        const int64_t i = base + lane + 64 * u;
+        v[u] = __builtin_nontemporal_load(a + (i < n16 ? i : n16 - 1));
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kOnceLoads; ++u)
+        s += __builtin_bit_cast(float, v[u].x) + __builtin_bit_cast(float, v[u].w);
+    if (s == -1234.5f)
+        out[blockIdx.x] = s;
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ a, u32x4 *__restrict__ b, int64_t n16)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -54,6 +79,20 @@ int hbm_read_probe(const void *buf, int64_t nbytes, float *out, int blocks, void
     void *args[] = {&a, &n16, &out};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&read_probe_kernel), dim3(blocks), dim3(256), args,
                                    0, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? 0 : (int)e;
+}
+
+int hbm_read_once_blocks(int64_t nbytes) { return nbytes <= 0 ? -1 : (int)((nbytes / 16 + 64 * kOnceLoads * 4 - 1) / (64 * kOnceLoads * 4)); }
+
+int hbm_read_once(const void *buf, int64_t nbytes, float *out, void *hip_stream)
+{
+    if (!buf || !out || nbytes <= 0 || nbytes % 16 || !ok16(buf) || nbytes > (int64_t(1) << 40))
+        return -1;
+    int64_t n16 = nbytes / 16;
+    const u32x4 *a = static_cast<const u32x4 *>(buf);
+    void *args[] = {&a, &n16, &out};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&read_once_kernel), dim3(hbm_read_once_blocks(nbytes)),
+                                   dim3(256), args, 0, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? 0 : (int)e;
 }
 

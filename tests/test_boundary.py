@@ -35,6 +35,22 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_every_declared_function():
+    import ctypes
+    from decode_gemv_elementwise_amd import build as bld
+    text = open(os.path.join(ROOT, "include", "hbm_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(hbm_[a-z_]+)\s*\(", text)))
+    assert {"hbm_read_probe", "hbm_read_once", "hbm_read_once_blocks", "hbm_copy"} <= set(names)
+    lib = ctypes.CDLL(bld.PROBE_LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.hbm_read_once_blocks.argtypes = [ctypes.c_int64]
+    assert lib.hbm_read_once_blocks(16) == 1
+    assert lib.hbm_read_once_blocks(32768) == 1 and lib.hbm_read_once_blocks(32784) == 2
+    assert lib.hbm_read_once_blocks(0) == -1
+
+
 def test_status_strings():
     for code in S.values():
         assert b.gemv_strerror(code)
