@@ -281,9 +281,9 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
     constexpr int NU = SW / SPU;             // W load units per lane
     // units issued before the pieces are ready (measured per format): f16
     // has nothing to do meanwhile and issues all; the 4-bit unpack is the
-    // longest, and it overlaps the stream best when most units are issued
-    // one ahead of their use
-    constexpr int PU = is16<FMT>() ? NU : (FMT == GEMV_W_Q4B32 ? NU / 4 : NU / 2);
+    // longest, and with 16 units per lane it overlaps the stream best when
+    // three quarters are issued one ahead of their use (with 8, half)
+    constexpr int PU = is16<FMT>() ? NU : (FMT == GEMV_W_Q4B32 ? (NU >= 16 ? NU / 4 : NU / 2) : NU / 2);
     constexpr int NSU = kBlock ? SW / 8 : 1; // scale units per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
