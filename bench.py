@@ -283,30 +283,32 @@ def probe_bandwidth(torch, nbytes=2 << 30):
     return nbytes / sec / 1e9, ok
 
 
-def read_once_us(torch, nbytes, steps, warmup):
+def read_once_us(torch, nbytes, steps, warmup, store=False):
     """Per-launch time of a kernel that only reads nbytes (one pass, every
     load issued at once), over rotating buffers totalling more than 512 MiB
     and replayed as a graph on its own stream, like the GEMV timing: the
-    shortest launch any kernel reading that many bytes can have here."""
+    shortest launch any kernel reading that many bytes can have here.  With
+    store, every wave also writes one result at the end, as a GEMV must."""
     import ctypes
     from decode_gemv_elementwise_amd import build as b
     lib = ctypes.CDLL(b.PROBE_LIB)
-    lib.hbm_read_once.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    fn = lib.hbm_read_once_store if store else lib.hbm_read_once
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.hbm_read_once_blocks.argtypes = [ctypes.c_int64]
     nbytes = (nbytes + 15) // 16 * 16
     slot = (nbytes + 4095) // 4096 * 4096
     copies = max(2, -(-(512 << 20) // slot))
     buf = torch.ones(copies * slot // 4, dtype=torch.float32, device="cuda")
-    out = torch.zeros(lib.hbm_read_once_blocks(nbytes), dtype=torch.float32, device="cuda")
+    out = torch.zeros(4 * lib.hbm_read_once_blocks(nbytes), dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         s = stream.cuda_stream
-        assert lib.hbm_read_once(buf.data_ptr(), nbytes, out.data_ptr(), s) == 0
+        assert fn(buf.data_ptr(), nbytes, out.data_ptr(), s) == 0
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for i in range(warmup + steps):
-                lib.hbm_read_once(buf.data_ptr() + (i % copies) * slot, nbytes, out.data_ptr(), s)
+                fn(buf.data_ptr() + (i % copies) * slot, nbytes, out.data_ptr(), s)
         g.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -517,6 +519,10 @@ def bench_workload(torch, binding, synth, name, args, probe):
         floor_us = read_once_us(torch, dom_bytes, args.steps, args.warmup)
         res["roofline"]["same_size_read_us"] = round(floor_us, 3)
         res["roofline"]["frac_of_same_size_read"] = round(floor_us / (dom_sec * 1e6), 4)
+        # ... and then one store per wave, which every GEMV launch also waits for
+        floor_st_us = read_once_us(torch, dom_bytes, args.steps, args.warmup, store=True)
+        res["roofline"]["same_size_read_store_us"] = round(floor_st_us, 3)
+        res["roofline"]["frac_of_same_size_read_store"] = round(floor_st_us / (dom_sec * 1e6), 4)
     del step
     torch.cuda.empty_cache()
     return res, wl

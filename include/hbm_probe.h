@@ -31,6 +31,13 @@ int hbm_read_probe(const void *buf, int64_t nbytes, float *out, int blocks, void
 int hbm_read_once(const void *buf, int64_t nbytes, float *out, void *hip_stream);
 int hbm_read_once_blocks(int64_t nbytes);
 
+/* The same read, then one 4-byte store per wave (its sum, reduced over its
+ * lanes) to out[wave]: a launch ends only when its stores are acknowledged,
+ * so this is the floor for a kernel that reads nbytes and writes a result
+ * per wave, as a GEMV does.  out must hold 4 * hbm_read_once_blocks(nbytes)
+ * floats. */
+int hbm_read_once_store(const void *buf, int64_t nbytes, float *out, void *hip_stream);
+
 /* dst[0..nbytes) = src[0..nbytes) with 128-bit loads and stores; nbytes a
  * positive multiple of 16, both pointers 16-byte aligned, no overlap. */
 int hbm_copy(const void *src, void *dst, int64_t nbytes, void *hip_stream);

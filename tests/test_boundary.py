@@ -41,7 +41,7 @@ def test_probe_library_exports_every_declared_function():
     text = open(os.path.join(ROOT, "include", "hbm_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(hbm_[a-z_]+)\s*\(", text)))
-    assert {"hbm_read_probe", "hbm_read_once", "hbm_read_once_blocks", "hbm_copy"} <= set(names)
+    assert {"hbm_read_probe", "hbm_read_once", "hbm_read_once_blocks", "hbm_read_once_store", "hbm_copy"} <= set(names)
     lib = ctypes.CDLL(bld.PROBE_LIB)
     for n in names:
         assert hasattr(lib, n), n
