@@ -207,6 +207,29 @@ def ncols_reference(fmt, N, K, w, X, act, M=None, R=None, rows=None):
     return Y, acc, absacc
 
 
+def glu_ncols_reference(fmt, N, K, w_gate, w_up, X, act="silu", rows=None):
+    """The gated pair over several destination columns: column b is the
+    one-column gated pair of x_b = X[b], y_b = act(W_gate x_b) * (W_up x_b).
+    The gate path of "feat(cuda): fuse activations and residual add into mmv
+    f/q epilogues" (Summary) is stated for one destination column; this is
+    its plain widening to ncols columns, each column computed exactly as a
+    separate one-column call.
+
+    X is float32 [ncols, K].  Returns (Y, G, absG, U, absU), each float64
+    [ncols, rows]; row b of each is destination column b (dst[b * N + i])."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim != 2 or X.shape[1] != K:
+        raise ValueError("X must be float32 [ncols, K]")
+    B = X.shape[0]
+    b0, e0 = (0, N) if rows is None else rows
+    out = [np.empty((B, e0 - b0)) for _ in range(5)]
+    for b in range(B):
+        res = glu_reference(fmt, N, K, w_gate, w_up, X[b], act, rows=(b0, e0))
+        for o, v in zip(out, res):
+            o[b] = v
+    return tuple(out)
+
+
 def fwht_signed(x, s, n):
     """Signed Hadamard transform of every row of x ([K] or [rows, K] float32):
     y = n^-1/2 H_n (x * s) per block of n, the sign of element k being

@@ -388,6 +388,36 @@ def test_glu_closed_forms():
         oracle.glu_epilogue("add", u, u)
 
 
+def test_glu_ncols_closed_forms_and_column_order():
+    """Identity gate and up over several columns: column b is act(x_b) * x_b
+    (scipy's logistic); zero up gives 0 everywhere; reversing the columns of X
+    reverses the columns of the result; one column is the one-column pair."""
+    rng = np.random.default_rng(52)
+    N = K = 64
+    B = 5
+    X = np.stack([synth.draw_vec(rng, K) for _ in range(B)])
+    eye = np.eye(N, K, dtype=np.float16).view(np.uint8).reshape(-1)
+    zero = np.zeros(N * K, dtype=np.float16).view(np.uint8)
+    Xd = X.astype(np.float64)
+    Y, G, _, U, _ = oracle.glu_ncols_reference("f16", N, K, eye, eye, X, "silu")
+    assert np.allclose(Y, Xd * scipy.special.expit(Xd) * Xd, rtol=1e-15, atol=0)
+    assert np.array_equal(G, Xd) and np.array_equal(U, Xd)
+    Y, *_ = oracle.glu_ncols_reference("f16", N, K, eye, eye, X, "sigmoid")
+    assert np.allclose(Y, scipy.special.expit(Xd) * Xd, rtol=1e-15, atol=0)
+    Y, *_ = oracle.glu_ncols_reference("f16", N, K, eye, zero, X, "silu")
+    assert np.all(Y == 0.0)
+    wg = synth.random_weights(rng, "q4b32", N, K)
+    wu = synth.random_weights(rng, "q4b32", N, K)
+    Y, *_ = oracle.glu_ncols_reference("q4b32", N, K, wg.data, wu.data, X, "silu")
+    Yr, *_ = oracle.glu_ncols_reference("q4b32", N, K, wg.data, wu.data, X[::-1], "silu")
+    assert np.array_equal(Yr, Y[::-1])
+    y1, *_ = oracle.glu_reference("q4b32", N, K, wg.data, wu.data, X[2], "silu")
+    Y1, *_ = oracle.glu_ncols_reference("q4b32", N, K, wg.data, wu.data, X[2:3], "silu")
+    assert np.array_equal(Y1[0], y1)
+    Ys, *_ = oracle.glu_ncols_reference("q4b32", N, K, wg.data, wu.data, X, "silu", rows=(7, 30))
+    assert np.array_equal(Ys, Y[:, 7:30])
+
+
 def test_glu_metric_scale():
     g = np.array([0.0, 1.5, -2.0])
     u = np.array([2.0, -1.0, 0.5])
