@@ -62,6 +62,10 @@ def load(path=None):
     lib.gemv_glu.restype = ctypes.c_int
     lib.gemv_glu_validate.argtypes = [_VP, _VP, ctypes.c_int, _I64, _I64, _VP, ctypes.c_int, _VIEWP]
     lib.gemv_glu_validate.restype = ctypes.c_int
+    lib.gemv_glu_ncols.argtypes = [_VP, _VP, ctypes.c_int, _I64, _I64, _I64, _VP, ctypes.c_int, _VIEWP, _VP]
+    lib.gemv_glu_ncols.restype = ctypes.c_int
+    lib.gemv_glu_ncols_validate.argtypes = [_VP, _VP, ctypes.c_int, _I64, _I64, _I64, _VP, ctypes.c_int, _VIEWP]
+    lib.gemv_glu_ncols_validate.restype = ctypes.c_int
     lib.gemv_fused_ncols.argtypes = [_VP, ctypes.c_int, _I64, _I64, _I64, _VP, ctypes.c_int, _VIEWP, _VIEWP,
                                      _VIEWP, _VP]
     lib.gemv_fused_ncols.restype = ctypes.c_int
@@ -208,6 +212,20 @@ def gemv_glu(W_gate, W_up, wfmt, N, K, x, act="silu", dst=None, stream=None):
 def gemv_glu_validate(W_gate, W_up, wfmt, N, K, x, act="silu", dst=None) -> int:
     return load().gemv_glu_validate(_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, _addr(x), _act(act),
                                     _as_view(dst))
+
+
+def gemv_glu_ncols(W_gate, W_up, wfmt, N, K, ncols, x, act="silu", dst=None, stream=None):
+    """dst[b, i] = act((W_gate x_b)_i) * (W_up x_b)_i for ncols columns x_b =
+    x[b] (x: [ncols, K] f32; dst: ncols * N f32 in [ncols][N] order), one launch."""
+    st = load().gemv_glu_ncols(_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, ncols, _addr(x), _act(act),
+                               _as_view(dst), _stream(stream))
+    if st != 0:
+        _raise(st)
+
+
+def gemv_glu_ncols_validate(W_gate, W_up, wfmt, N, K, ncols, x, act="silu", dst=None) -> int:
+    return load().gemv_glu_ncols_validate(_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, ncols, _addr(x), _act(act),
+                                          _as_view(dst))
 
 
 def gemv_fused_ncols(W, wfmt, N, K, ncols, x, act, mul_operand=None, add_operand=None, dst=None, stream=None):

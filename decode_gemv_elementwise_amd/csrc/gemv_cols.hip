@@ -66,7 +66,7 @@ namespace {
 // every column staged once, every W chunk of the wave's rows issued at once),
 // used when that fits LDS; 8 waves of 2 rows (16 rows per workgroup) keep
 // 2 * UO loads per lane in flight.
-template <int FMT, int NC, int UO = 0> struct ColsCfg {
+template <int FMT, int NC, int UO = 0, bool GLU = false> struct ColsCfg {
     static constexpr int E = Fmt<FMT>::E;
     static constexpr int kWaves = UO > 0 ? 8 : GEMV_COLS_WAVES;
     // chunks per lane per segment: GEMV_COLS_X_BUDGET / (NC * E), 1..8 (a
@@ -74,8 +74,10 @@ template <int FMT, int NC, int UO = 0> struct ColsCfg {
     static constexpr int kU0 = GEMV_COLS_X_BUDGET / (NC * E);
     static constexpr int U = UO > 0 ? UO : (kU0 < 1 ? 1 : (kU0 > 8 ? 8 : kU0));
     // rows per wave: about GEMV_COLS_LOADS chunk loads per lane per batch, 1..4
+    // (a gated pair loads a gate and an up row per output row: half as many)
     static constexpr int kR0 = GEMV_COLS_LOADS / U;
-    static constexpr int R = UO > 0 ? 2 : (kR0 > 4 ? 4 : (kR0 < 1 ? 1 : kR0));
+    static constexpr int kR1 = UO > 0 ? 2 : (kR0 > 4 ? 4 : (kR0 < 1 ? 1 : kR0));
+    static constexpr int R = GLU ? (kR1 > 1 ? kR1 / 2 : 1) : kR1;
     static constexpr int SEG = 64 * U * E;     // x floats per column per segment
     static constexpr int kPlane4 = SEG / 4;    // float4 slots per plane (a multiple of 64)
     static constexpr int kBuf4 = NC * kPlane4; // float4 slots per segment buffer
@@ -173,14 +175,17 @@ __device__ __forceinline__ void consume_cols(const Batch<FMT, R, U> &b, const f3
     }
 }
 
-template <int FMT, int NC, int UO>
-__global__ __launch_bounds__((ColsCfg<FMT, NC, UO>::kWaves * kWave)) void gemv_cols_kernel(
+// GLU: the gated pair; W2 is the up matrix, act the gate's (SILU or
+// SIGMOID), and each wave loads its R gate rows and the same R up rows.
+template <int FMT, int NC, int UO, bool GLU = false>
+__global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void gemv_cols_kernel(
     const unsigned char *__restrict__ W, const float *__restrict__ x, int N, int K, int act, const float *mop,
-    const float *rop, float *dst)
+    const float *rop, float *dst, const unsigned char *__restrict__ W2)
 {
     using F = Fmt<FMT>;
-    using C = ColsCfg<FMT, NC, UO>;
+    using C = ColsCfg<FMT, NC, UO, GLU>;
     constexpr int R = C::R, U = C::U, SEGC = kWave * C::U;
+    constexpr int RR = GLU ? 2 * R : R; // rows loaded per wave
     // two segment buffers (x of segment s+1 lands in one while segment s is
     // read from the other); a row of one segment gets only the first
     extern __shared__ f32x4 lds4[];
@@ -194,6 +199,7 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO>::kWaves * kWave)) void gemv_c
     const int row0 = (blockIdx.x * C::kWaves + wave) * R;
     const int64_t rbytes = row_bytes<FMT>(K);
     const unsigned char *scales = F::kBlock ? W + align256_dev((int64_t)N * rbytes) : nullptr;
+    const unsigned char *scales2 = (F::kBlock && GLU) ? W2 + align256_dev((int64_t)N * rbytes) : nullptr;
     const int64_t sbytes = (int64_t)(K / 32) * 2;
 
     // 1. epilogue operand of the output this lane finishes (lane j: row
@@ -209,21 +215,25 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO>::kWaves * kWave)) void gemv_c
     dma_x_segment<FMT, NC, UO>(xa, x, K, 0, wave, lane, x16);
 
     // 3. W, first batch
-    const unsigned char *wrow[R];
-    const unsigned char *srow[R];
+    const unsigned char *wrow[RR];
+    const unsigned char *srow[RR];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int row = min(row0 + r, N - 1);
         wrow[r] = W + (int64_t)row * rbytes;
         srow[r] = F::kBlock ? scales + (int64_t)row * sbytes : nullptr;
+        if constexpr (GLU) {
+            wrow[R + r] = W2 + (int64_t)row * rbytes;
+            srow[R + r] = F::kBlock ? scales2 + (int64_t)row * sbytes : nullptr;
+        }
     }
-    Batch<FMT, R, U> b0, b1;
+    Batch<FMT, RR, U> b0, b1;
     if constexpr (UO == 0) // one-shot: W follows the wait for x (below)
-        issue_batch<FMT, R, U>(b0, wrow, srow, lane, 0, nchunks);
+        issue_batch<FMT, RR, U>(b0, wrow, srow, lane, 0, nchunks);
 
-    float acc[R][NC];
+    float acc[RR][NC];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RR; ++r)
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             acc[r][c] = 0.0f;
@@ -240,26 +250,26 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO>::kWaves * kWave)) void gemv_c
         // lands (the copy's wait would otherwise have waited for all of W)
         __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0); expcnt, lgkmcnt not waited for
         __builtin_amdgcn_s_barrier();
-        issue_batch<FMT, R, U>(b0, wrow, srow, lane, 0, nchunks);
-        consume_cols<FMT, NC, UO, R, U>(b0, xa, acc, lane, 0, nchunks);
+        issue_batch<FMT, RR, U>(b0, wrow, srow, lane, 0, nchunks);
+        consume_cols<FMT, NC, UO, RR, U>(b0, xa, acc, lane, 0, nchunks);
     } else
     for (int s = 0;;) {
         __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0); expcnt, lgkmcnt not waited for
         __builtin_amdgcn_s_barrier();
         if (s + 1 < nseg) {
             dma_x_segment<FMT, NC, UO>(xb, x, K, s + 1, wave, lane, x16);
-            issue_batch<FMT, R, U>(b1, wrow, srow, lane, (s + 1) * U, nchunks);
+            issue_batch<FMT, RR, U>(b1, wrow, srow, lane, (s + 1) * U, nchunks);
         }
-        consume_cols<FMT, NC, UO, R, U>(b0, xa, acc, lane, s * SEGC, nchunks);
+        consume_cols<FMT, NC, UO, RR, U>(b0, xa, acc, lane, s * SEGC, nchunks);
         if (++s == nseg)
             break;
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __builtin_amdgcn_s_barrier();
         if (s + 1 < nseg) {
             dma_x_segment<FMT, NC, UO>(xa, x, K, s + 1, wave, lane, x16);
-            issue_batch<FMT, R, U>(b0, wrow, srow, lane, (s + 1) * U, nchunks);
+            issue_batch<FMT, RR, U>(b0, wrow, srow, lane, (s + 1) * U, nchunks);
         }
-        consume_cols<FMT, NC, UO, R, U>(b1, xb, acc, lane, s * SEGC, nchunks);
+        consume_cols<FMT, NC, UO, RR, U>(b1, xb, acc, lane, s * SEGC, nchunks);
         if (++s == nseg)
             break;
     }
@@ -270,10 +280,12 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO>::kWaves * kWave)) void gemv_c
     for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float sum = wave_sum(acc[r][c]);
+            float sum = wave_sum(acc[r][c]);
+            if constexpr (GLU)
+                sum = apply_glu(act, sum, wave_sum(acc[R + r][c]));
             mine = lane == c * R + r ? sum : mine;
         }
-    const float y = apply_epilogue(act, mine, opv);
+    const float y = GLU ? mine : apply_epilogue(act, mine, opv);
     if (lane < R * NC && row0 + lane % R < N)
         dst[(int64_t)(lane / R) * N + row0 + lane % R] = y;
 }
@@ -304,35 +316,48 @@ __device__ __forceinline__ float weight_at_cols(const unsigned char *W, int N, i
     }
 }
 
-template <int FMT, int NC>
+template <int FMT, int NC, bool GLU = false>
 __global__ __launch_bounds__(256) void gemv_cols_generic_kernel(const unsigned char *__restrict__ W,
                                                                 const float *__restrict__ x, int N, int K, int act,
-                                                                const float *mop, const float *rop, float *dst)
+                                                                const float *mop, const float *rop, float *dst,
+                                                                const unsigned char *__restrict__ W2)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int nwaves = gridDim.x * (blockDim.x / kWave);
     for (int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; row < N; row += nwaves) {
-        float acc[NC];
+        float acc[NC], acc2[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-            acc[c] = 0.0f;
+            acc[c] = acc2[c] = 0.0f;
         for (int k = lane; k < K; k += kWave) {
             const float w = weight_at_cols<FMT>(W, N, K, row, k);
 #pragma unroll
             for (int c = 0; c < NC; ++c)
                 acc[c] = fmaf(w, x[(int64_t)c * K + k], acc[c]);
+            if constexpr (GLU) {
+                const float w2 = weight_at_cols<FMT>(W2, N, K, row, k);
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    acc2[c] = fmaf(w2, x[(int64_t)c * K + k], acc2[c]);
+            }
         }
         float mine = 0.0f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const float sum = wave_sum(acc[c]);
+            float sum = wave_sum(acc[c]);
+            if constexpr (GLU)
+                sum = apply_glu(act, sum, wave_sum(acc2[c]));
             mine = lane == c ? sum : mine;
         }
         if (lane < NC) {
             const int64_t o = (int64_t)lane * N + row;
-            const bool has_op = act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL || act == GEMV_ACT_ADD;
-            const float v = has_op ? (act == GEMV_ACT_ADD ? rop[o] : mop[o]) : 0.0f;
-            dst[o] = apply_epilogue(act, mine, v);
+            if constexpr (GLU) {
+                dst[o] = mine;
+            } else {
+                const bool has_op = act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL || act == GEMV_ACT_ADD;
+                const float v = has_op ? (act == GEMV_ACT_ADD ? rop[o] : mop[o]) : 0.0f;
+                dst[o] = apply_epilogue(act, mine, v);
+            }
         }
     }
 }
@@ -341,10 +366,10 @@ __global__ __launch_bounds__(256) void gemv_cols_generic_kernel(const unsigned c
 
 using ColsCall = ColsArgs;
 
-template <int FMT, int NC, int UO> hipError_t launch_cols(const ColsCall &c, hipStream_t s)
+template <int FMT, int NC, int UO, bool GLU = false> hipError_t launch_cols(const ColsCall &c, hipStream_t s)
 {
-    using C = ColsCfg<FMT, NC, UO>;
-    const void *fn = reinterpret_cast<const void *>(&gemv_cols_kernel<FMT, NC, UO>);
+    using C = ColsCfg<FMT, NC, UO, GLU>;
+    const void *fn = reinterpret_cast<const void *>(&gemv_cols_kernel<FMT, NC, UO, GLU>);
     const int nchunks = c.K / C::E;
     const int nseg = (nchunks + kWave * C::U - 1) / (kWave * C::U);
     const size_t lds = (size_t)(nseg > 1 ? 2 : 1) * C::kBuf4 * 16;
@@ -362,13 +387,14 @@ template <int FMT, int NC, int UO> hipError_t launch_cols(const ColsCall &c, hip
     int N = c.N, K = c.K, act = c.act;
     const float *m = c.m, *r = c.r;
     float *dst = c.dst;
-    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst};
+    const unsigned char *W2 = c.W2;
+    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst, &W2};
     return hipLaunchKernel(fn, dim3(grid), dim3(C::kWaves * kWave), args, lds, s);
 }
 
-template <int FMT, int NC> hipError_t launch_cols_generic(const ColsCall &c, hipStream_t s)
+template <int FMT, int NC, bool GLU = false> hipError_t launch_cols_generic(const ColsCall &c, hipStream_t s)
 {
-    const void *fn = reinterpret_cast<const void *>(&gemv_cols_generic_kernel<FMT, NC>);
+    const void *fn = reinterpret_cast<const void *>(&gemv_cols_generic_kernel<FMT, NC, GLU>);
     int grid = (c.N + 3) / 4;
     if (grid > 65536)
         grid = 65536;
@@ -377,7 +403,8 @@ template <int FMT, int NC> hipError_t launch_cols_generic(const ColsCall &c, hip
     int N = c.N, K = c.K, act = c.act;
     const float *m = c.m, *r = c.r;
     float *dst = c.dst;
-    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst};
+    const unsigned char *W2 = c.W2;
+    void *args[] = {&W, &x, &N, &K, &act, &m, &r, &dst, &W2};
     return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, s);
 }
 
@@ -391,12 +418,12 @@ template <int FMT, int NC> hipError_t launch_cols_generic(const ColsCall &c, hip
 // block formats, 2048 for f32).
 template <int FMT> constexpr int oneshot_u() { return Fmt<FMT>::E <= 8 ? 8 : (Fmt<FMT>::E == 16 ? 4 : 2); }
 
-template <int FMT, int NC> hipError_t dispatch_cols(const ColsCall &c, hipStream_t s)
+template <int FMT, int NC, bool GLU = false> hipError_t dispatch_cols(const ColsCall &c, hipStream_t s)
 {
     const int64_t lds1 = (int64_t)(c.K / Fmt<FMT>::E) * Fmt<FMT>::XS * 4;
     const bool fast = (row_bytes<FMT>(c.K) % 16 == 0) && lds1 <= kMaxLds;
     if (!fast)
-        return launch_cols_generic<FMT, NC>(c, s);
+        return launch_cols_generic<FMT, NC, GLU>(c, s);
     constexpr int UO = oneshot_u<FMT>();
     const int cpl = (c.K / Fmt<FMT>::E + kWave - 1) / kWave;
     if constexpr (NC * kWave * UO * Fmt<FMT>::E * 4 <= kMaxLds) {
@@ -409,44 +436,44 @@ template <int FMT, int NC> hipError_t dispatch_cols(const ColsCall &c, hipStream
         const bool take = Fmt<FMT>::kBlock ||
                           (NC >= 3 && wgs >= cus && (lds <= 64 * 1024 || wgs <= cus));
         if (GEMV_COLS_ONESHOT && cpl <= UO && take)
-            return launch_cols<FMT, NC, UO>(c, s);
+            return launch_cols<FMT, NC, UO, GLU>(c, s);
     }
-    return launch_cols<FMT, NC, 0>(c, s);
+    return launch_cols<FMT, NC, 0, GLU>(c, s);
 }
 
-template <int NC> hipError_t dispatch_cols_fmt(int wfmt, const ColsCall &c, hipStream_t s)
+template <int NC, bool GLU = false> hipError_t dispatch_cols_fmt(int wfmt, const ColsCall &c, hipStream_t s)
 {
     switch (wfmt) {
     case GEMV_W_F32:
-        return dispatch_cols<GEMV_W_F32, NC>(c, s);
+        return dispatch_cols<GEMV_W_F32, NC, GLU>(c, s);
     case GEMV_W_F16:
-        return dispatch_cols<GEMV_W_F16, NC>(c, s);
+        return dispatch_cols<GEMV_W_F16, NC, GLU>(c, s);
     case GEMV_W_BF16:
-        return dispatch_cols<GEMV_W_BF16, NC>(c, s);
+        return dispatch_cols<GEMV_W_BF16, NC, GLU>(c, s);
     case GEMV_W_Q8B32:
-        return dispatch_cols<GEMV_W_Q8B32, NC>(c, s);
+        return dispatch_cols<GEMV_W_Q8B32, NC, GLU>(c, s);
     default:
-        return dispatch_cols<GEMV_W_Q4B32, NC>(c, s);
+        return dispatch_cols<GEMV_W_Q4B32, NC, GLU>(c, s);
     }
 }
 
-hipError_t dispatch_ncols(int wfmt, int ncols, const ColsCall &c, hipStream_t s)
+template <bool GLU = false> hipError_t dispatch_ncols(int wfmt, int ncols, const ColsCall &c, hipStream_t s)
 {
     switch (ncols) {
     case 2:
-        return dispatch_cols_fmt<2>(wfmt, c, s);
+        return dispatch_cols_fmt<2, GLU>(wfmt, c, s);
     case 3:
-        return dispatch_cols_fmt<3>(wfmt, c, s);
+        return dispatch_cols_fmt<3, GLU>(wfmt, c, s);
     case 4:
-        return dispatch_cols_fmt<4>(wfmt, c, s);
+        return dispatch_cols_fmt<4, GLU>(wfmt, c, s);
     case 5:
-        return dispatch_cols_fmt<5>(wfmt, c, s);
+        return dispatch_cols_fmt<5, GLU>(wfmt, c, s);
     case 6:
-        return dispatch_cols_fmt<6>(wfmt, c, s);
+        return dispatch_cols_fmt<6, GLU>(wfmt, c, s);
     case 7:
-        return dispatch_cols_fmt<7>(wfmt, c, s);
+        return dispatch_cols_fmt<7, GLU>(wfmt, c, s);
     default:
-        return dispatch_cols_fmt<8>(wfmt, c, s);
+        return dispatch_cols_fmt<8, GLU>(wfmt, c, s);
     }
 }
 
@@ -502,6 +529,20 @@ int gemv_fused_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncol
     }
     return gemv::finish_launch(
         (int)gemv::dispatch_ncols(wfmt, (int)ncols, c, static_cast<hipStream_t>(hip_stream)));
+}
+
+int gemv_glu_ncols(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, int64_t ncols,
+                   const float *x, int act, const gemv_view *dst, void *hip_stream)
+{
+    int st = gemv::validate_glu_ncols(W_gate, W_up, wfmt, N, K, ncols, x, act, dst);
+    if (st != GEMV_OK)
+        return st;
+    if (ncols == 1)
+        return gemv_glu(W_gate, W_up, wfmt, N, K, x, act, dst, hip_stream);
+    gemv::ColsCall c{static_cast<const unsigned char *>(W_gate), x, (int)N, (int)K, act, nullptr, nullptr,
+                     dst->data, static_cast<const unsigned char *>(W_up)};
+    return gemv::finish_launch(
+        (int)gemv::dispatch_ncols<true>(wfmt, (int)ncols, c, static_cast<hipStream_t>(hip_stream)));
 }
 
 } // extern "C"

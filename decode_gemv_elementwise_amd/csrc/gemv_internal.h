@@ -17,6 +17,8 @@ int validate_epilogue(int act, int64_t N, const float *acc, const gemv_view *mul
                       const gemv_view *add_operand, const gemv_view *dst);
 int validate_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,
                  const gemv_view *dst);
+int validate_glu_ncols(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, int64_t ncols,
+                       const float *x, int act, const gemv_view *dst);
 const char *strerror_of(int status);
 int validate_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncols, const float *x, int act,
                    const gemv_view *mul_operand, const gemv_view *add_operand, const gemv_view *dst);
@@ -34,6 +36,7 @@ struct ColsArgs {
     int N, K, act;
     const float *m, *r;
     float *dst;
+    const unsigned char *W2 = nullptr; // up matrix of a gated pair (act is the gate's)
 };
 
 // The matrix-core column kernels (16-bit and block formats).  The plan: tiles

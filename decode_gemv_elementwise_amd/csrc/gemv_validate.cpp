@@ -190,23 +190,37 @@ int validate(const void *W, int wfmt, int64_t N, int64_t K, const float *x, int 
 int validate_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,
                  const gemv_view *dst)
 {
+    return validate_glu_ncols(W_gate, W_up, wfmt, N, K, 1, x, act, dst);
+}
+
+// The gated pair over ncols destination columns: x is [ncols][K], dst holds
+// ncols * N values; otherwise the rules of the one-column pair.
+int validate_glu_ncols(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, int64_t ncols,
+                       const float *x, int act, const gemv_view *dst)
+{
     if (!W_gate || !W_up || !x)
         return GEMV_E_NULL;
     if (wfmt < GEMV_W_F32 || wfmt > GEMV_W_Q4B32)
         return GEMV_E_FMT;
     if (act != GEMV_ACT_SILU && act != GEMV_ACT_SIGMOID)
         return GEMV_E_ACT;
+    if (ncols < 1 || ncols > GEMV_MAX_NCOLS)
+        return GEMV_E_DIM;
     int64_t wbytes = weight_bytes(wfmt, N, K);
     if (wbytes < 0)
         return static_cast<int>(wbytes);
+    const int64_t nout = N * ncols; // N < 2^31 and ncols <= 8: no overflow
+    if (nout >= GEMV_MAX_DIM_EXTENT)
+        return GEMV_E_DIM;
     const gemv_view *operand = nullptr;
-    int st = check_epilogue_views(GEMV_ACT_NONE, N, nullptr, nullptr, dst, &operand);
+    int st = check_epilogue_views(GEMV_ACT_NONE, nout, nullptr, nullptr, dst, &operand);
     if (st != GEMV_OK)
         return st;
     if (!aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(x, 4))
         return GEMV_E_ALIGN;
-    Span sd = span_of(dst->data, N * 4);
-    if (overlap(sd, span_of(W_gate, wbytes)) || overlap(sd, span_of(W_up, wbytes)) || overlap(sd, span_of(x, K * 4)))
+    Span sd = span_of(dst->data, nout * 4);
+    if (overlap(sd, span_of(W_gate, wbytes)) || overlap(sd, span_of(W_up, wbytes)) ||
+        overlap(sd, span_of(x, ncols * K * 4)))
         return GEMV_E_ALIAS;
     return GEMV_OK;
 }
@@ -362,6 +376,12 @@ int gemv_epilogue_validate(int act, int64_t N, const float *acc, const gemv_view
                            const gemv_view *add_operand, const gemv_view *dst)
 {
     return gemv::validate_epilogue(act, N, acc, mul_operand, add_operand, dst);
+}
+
+int gemv_glu_ncols_validate(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, int64_t ncols,
+                            const float *x, int act, const gemv_view *dst)
+{
+    return gemv::validate_glu_ncols(W_gate, W_up, wfmt, N, K, ncols, x, act, dst);
 }
 
 int gemv_glu_validate(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,

@@ -170,6 +170,24 @@ int gemv_fused(const void *W, int wfmt, int64_t N, int64_t K, const float *x, in
 int gemv_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x, int act,
              const gemv_view *dst, void *hip_stream);
 
+/* The gated pair over 1..8 destination columns (small-batch or speculative
+ * decode), in one launch: column b of x ([ncols][K] f32) gives
+ *     dst[b * N + i] = act((W_gate x_b)_i) * (W_up x_b)_i
+ * with the matrices, act and alignment rules of gemv_glu; dst is an f32
+ * view holding ncols * N elements that overlaps neither matrix nor x.  Both
+ * matrices are read once for all columns; each chunk of a row is decoded
+ * once and multiplied into every column.  Each row sum is formed exactly as
+ * gemv_fused_ncols forms it on its vector-ALU column kernels, so column b
+ * equals gemv_glu on x_b bit for bit (ncols == 1 is gemv_glu).  Returns
+ * GEMV_OK or a negative status (GEMV_E_DIM for ncols outside 1..8);
+ * asynchronous on hip_stream; allocates nothing. */
+int gemv_glu_ncols(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, int64_t ncols,
+                   const float *x, int act, const gemv_view *dst, void *hip_stream);
+
+/* The host-side checks of gemv_glu_ncols; no HIP call. */
+int gemv_glu_ncols_validate(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, int64_t ncols,
+                            const float *x, int act, const gemv_view *dst);
+
 /* The host-side checks of gemv_glu; no HIP call. */
 int gemv_glu_validate(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, const float *x,
                       int act, const gemv_view *dst);
@@ -301,7 +319,7 @@ const char *gemv_strerror(int status);
 
 /* The hipError_t of the last failed launch on the calling thread (0 if
  * none); reset to 0 by every successful launching call (gemv_fused,
- * gemv_fused_ncols, gemv_glu, gemv_epilogue, gemv_fwht_signed,
+ * gemv_fused_ncols, gemv_glu, gemv_glu_ncols, gemv_epilogue, gemv_fwht_signed,
  * gemv_fused_fwht). */
 int gemv_last_hip_error(void);
 

@@ -189,6 +189,18 @@ int main(int argc, char **argv)
         const int sg = gemv_glu_validate(W, W2, wfmt, N, K, x, act, dp);
         if (!valid_status(sg) || sg != gemv_glu_validate(W, W2, wfmt, N, K, x, act, dp))
             fail("gemv_glu_validate status", it);
+        const int sgn = gemv_glu_ncols_validate(W, W2, wfmt, N, K, ncols, x, act, dp);
+        if (!valid_status(sgn) || sgn != gemv_glu_ncols_validate(W, W2, wfmt, N, K, ncols, x, act, dp))
+            fail("gemv_glu_ncols_validate status", it);
+        if (ncols == 1 && sgn != sg)
+            fail("gemv_glu_ncols_validate with one column and gemv_glu_validate disagree", it);
+        if (sgn == GEMV_OK) {
+            const u128 db = (u128)N * ncols * 4;
+            const uintptr_t d = reinterpret_cast<uintptr_t>(dp->data);
+            if (wref < 0 || !disjoint(d, db, (uintptr_t)W, (u128)wref) || !disjoint(d, db, (uintptr_t)W2, (u128)wref) ||
+                !disjoint(d, db, (uintptr_t)x, (u128)ncols * K * 4))
+                fail("gemv_glu_ncols_validate accepted dst overlapping a matrix or x", it);
+        }
         const int se = gemv_epilogue_validate(act, N, x, mp, ap, dp);
         if (!valid_status(se) || se != gemv_epilogue_validate(act, N, x, mp, ap, dp))
             fail("gemv_epilogue_validate status", it);
@@ -203,7 +215,7 @@ int main(int argc, char **argv)
         const int sp = gemv_fused_fwht_validate(W, wfmt, N, K, x, signs, n, nsigns, act, mp, ap, dp);
         if (!valid_status(sp) || sp != gemv_fused_fwht_validate(W, wfmt, N, K, x, signs, n, nsigns, act, mp, ap, dp))
             fail("gemv_fused_fwht_validate status", it);
-        for (int s : {s1, sc, sg, se, sf, sp})
+        for (int s : {s1, sc, sg, sgn, se, sf, sp})
             if (!gemv_strerror(s))
                 fail("gemv_strerror returned NULL", it);
     }

@@ -233,6 +233,38 @@ def test_glu_validate():
     assert gval(dst=v(X0, (64,))) == S["GEMV_E_ALIAS"]        # dst on x
 
 
+def gnval(ncols=4, **kw):
+    args = dict(Wg=W0, Wu=U0, wfmt="f16", N=64, K=64, x=X0, act="silu", dst=v(D0, (ncols, 64)))
+    args.update(kw)
+    return b.gemv_glu_ncols_validate(args["Wg"], args["Wu"], args["wfmt"], args["N"], args["K"], ncols,
+                                     args["x"], args["act"], args["dst"])
+
+
+def test_glu_ncols_validate():
+    assert gnval() == S["GEMV_OK"]
+    assert gnval(ncols=8, dst=v(D0, (8 * 64,))) == S["GEMV_OK"]
+    assert gnval(ncols=1, dst=v(D0, (64,))) == S["GEMV_OK"]
+    assert gnval(act="sigmoid") == S["GEMV_OK"]
+    for nc in (0, 9, -1):
+        assert gnval(ncols=nc, dst=v(D0, (64,))) == S["GEMV_E_DIM"]
+    assert gnval(dst=v(D0, (3, 64))) == S["GEMV_E_DIM"]                # dst holds 3 columns, not 4
+    for act in ("none", "silu_mul", "mul", "add"):
+        assert gnval(act=act) == S["GEMV_E_ACT"]
+    assert gnval(Wu=0) == S["GEMV_E_NULL"]
+    assert gnval(wfmt="q8b32", K=48) == S["GEMV_E_DIM"]
+    assert gnval(x=X0 + 2) == S["GEMV_E_ALIGN"]
+    # dst may not reach into any column of x, nor into either matrix
+    assert gnval(dst=v(X0 + 3 * 64 * 4, (4, 64))) == S["GEMV_E_ALIAS"]  # on x's fourth column
+    assert gnval(dst=v(X0 + 4 * 64 * 4, (4, 64))) == S["GEMV_OK"]       # just past x
+    assert gnval(dst=v(U0 + 64, (4, 64))) == S["GEMV_E_ALIAS"]
+    # one column is the one-column pair's check
+    for kw in (dict(), dict(act="none"), dict(Wu=U0 + 8), dict(dst=v(U0, (64,)))):
+        dst = kw.pop("dst", v(D0, (64,)))
+        a = gnval(ncols=1, dst=dst, **kw)
+        g = gval(dst=dst, **kw)
+        assert a == g, kw
+
+
 def nval(ncols=4, **kw):
     args = dict(W=W0, wfmt="f16", N=64, K=64, x=X0, act="none", mul_operand=None, add_operand=None,
                 dst=v(D0, (ncols, 64)))

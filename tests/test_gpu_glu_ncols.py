@@ -1,0 +1,108 @@
+"""The gated pair over several destination columns (gemv_glu_ncols) against
+the oracle, and against the one-column pair bit for bit: column b is
+act(W_gate x_b) * (W_up x_b), each row sum formed in the one-column order."""
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from oracle.compare import TOLERANCE, compare_glu
+from decode_gemv_elementwise_amd import binding, synth
+from gpu_util import dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 32), (33, 96), (300, 512), (1003, 4096), (67, 14336), (17, 4128)]
+
+
+def _run(wg, wu, X, act, out_shape=None):
+    B = X.shape[0]
+    Wg, Wu, Xd = dev(wg.data), dev(wu.data), dev(X)
+    dst = torch.full(out_shape or (B, wg.N), float("nan"), dtype=torch.float32, device="cuda")
+    binding.gemv_glu_ncols(Wg, Wu, wg.fmt, wg.N, wg.K, B, Xd, act, dst=dst)
+    torch.cuda.synchronize()
+    return host(dst).reshape(B, wg.N)
+
+
+def _one(wg, wu, x, act):
+    dst = torch.full((wg.N,), float("nan"), dtype=torch.float32, device="cuda")
+    binding.gemv_glu(dev(wg.data), dev(wu.data), wg.fmt, wg.N, wg.K, dev(x), act, dst=dst)
+    torch.cuda.synchronize()
+    return host(dst)
+
+
+def _check(wg, wu, X, act, tag):
+    log(f"glu ncols {tag} fmt={wg.fmt} N={wg.N} K={wg.K} ncols={X.shape[0]} act={act}")
+    G = _run(wg, wu, X, act)
+    Y, g, gA, u, uA = oracle.glu_ncols_reference(wg.fmt, wg.N, wg.K, wg.data, wu.data, X, act)
+    res = compare_glu(G.reshape(-1), Y.reshape(-1), act, g.reshape(-1), gA.reshape(-1), u.reshape(-1),
+                      uA.reshape(-1))
+    assert np.all(np.isfinite(G)), tag
+    assert res["max_err"] <= TOLERANCE[wg.fmt], f"{tag}: {res}"
+    return G
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_glu_ncols_parity(fmt, N, K):
+    rng = np.random.default_rng(zlib.crc32(f"gluncols/{fmt}/{N}/{K}".encode()))
+    wg = synth.random_weights(rng, fmt, N, K)
+    wu = synth.random_weights(rng, fmt, N, K)
+    for B, act in ((2, "silu"), (5, "sigmoid"), (8, "silu")):
+        X = np.stack([synth.draw_vec(rng, K) for _ in range(B)])
+        _check(wg, wu, X, act, f"{fmt} {N}x{K} {B} {act}")
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("N,K,B", [(300, 4096, 3), (67, 14336, 8), (17, 4128, 2), (1003, 512, 6)])
+def test_glu_ncols_columns_equal_one_column_pair_bitwise(fmt, N, K, B):
+    log(f"glu ncols == gemv_glu per column, {fmt} {N}x{K} ncols={B}")
+    rng = np.random.default_rng(zlib.crc32(f"glubit/{fmt}/{N}/{K}".encode()))
+    wg = synth.random_weights(rng, fmt, N, K)
+    wu = synth.random_weights(rng, fmt, N, K)
+    X = np.stack([synth.draw_vec(rng, K) for _ in range(B)])
+    G = _run(wg, wu, X, "silu")
+    for b in range(B):
+        assert np.array_equal(G[b].view(np.uint32), _one(wg, wu, X[b], "silu").view(np.uint32)), (fmt, b)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_glu_ncols_odd_k_generic_path(fmt):
+    log(f"glu ncols odd K {fmt}")
+    rng = np.random.default_rng(71)
+    wg = synth.random_weights(rng, fmt, 40, 1001)
+    wu = synth.random_weights(rng, fmt, 40, 1001)
+    X = np.stack([synth.draw_vec(rng, 1001) for _ in range(4)])
+    G = _check(wg, wu, X, "silu", f"{fmt} odd K")
+    for b in range(4):
+        assert np.array_equal(G[b].view(np.uint32), _one(wg, wu, X[b], "silu").view(np.uint32)), (fmt, b)
+
+
+def test_glu_ncols_full_size_gate_up():
+    """The 4-bit gate and up projections of the decode layer, 4 columns."""
+    rng = np.random.default_rng(72)
+    wl = synth.q4b32_decode_layer(0)
+    wg, wu = wl.weights["Wgate"], wl.weights["Wup"]
+    X = np.stack([synth.draw_vec(rng, wg.K) for _ in range(4)])
+    _check(wg, wu, X, "silu", "q4 14336x4096 gate/up")
+
+
+def test_glu_ncols_one_column_and_rejections():
+    log("glu ncols: one column, rejected calls")
+    rng = np.random.default_rng(73)
+    wg = synth.random_weights(rng, "bf16", 64, 256)
+    wu = synth.random_weights(rng, "bf16", 64, 256)
+    X = synth.draw_vec(rng, 256)[None, :]
+    assert np.array_equal(_run(wg, wu, X, "sigmoid")[0].view(np.uint32),
+                          _one(wg, wu, X[0], "sigmoid").view(np.uint32))
+    Wg, Wu, Xd = dev(wg.data), dev(wu.data), dev(np.stack([X[0]] * 3))
+    dst = torch.full((3, 64), 7.0, dtype=torch.float32, device="cuda")
+    for act, nc, status in (("add", 3, "GEMV_E_ACT"), ("silu", 9, "GEMV_E_DIM"), ("silu", 2, "GEMV_E_DIM")):
+        with pytest.raises(binding.GemvError) as e:
+            binding.gemv_glu_ncols(Wg, Wu, "bf16", 64, 256, nc, Xd, act, dst=dst)
+        assert e.value.status == binding.STATUS_CODE[status]
+    torch.cuda.synchronize()
+    assert torch.all(dst == 7.0)
