@@ -29,16 +29,49 @@ constexpr int kMaxLds = 160 * 1024; // LDS bytes a gfx950 workgroup may allocate
 // t / (1 + t) and a t / (1 + t).  (The direct form turns silu(a) into -0 once
 // e^-a overflows, near a = -88.7, although the true value is still a normal
 // float there.)
+//
+// Below a = -80, e^a (under 2e-35) is leaving float's normal range: on its
+// own it would round to zero or to a few subnormal bits before |a| and a
+// multiplier scale it back up (silu(-103) * 40 is about -5e-42, a float,
+// while e^-103 alone rounds to 0).  There the product f * e^a is formed
+// 2^64 times larger, where e^(a + 64 ln 2) is a normal float, and scaled
+// back once, so that it rounds into the subnormal range a single time;
+// 1 + e^a is 1 in float there.  -inf still gives silu NaN and sigmoid 0.
+constexpr float kTailA = -80.0f;
+constexpr float kLn2Times64 = 44.3614195558365f; // 64 ln 2
+
+__device__ __forceinline__ float tail_scaled(float f, float a) { return ldexpf(f * expf(a + kLn2Times64), -64); }
+
 __device__ __forceinline__ float sigmoid_f(float a)
 {
+    if (a < kTailA)
+        return tail_scaled(1.0f, a);
     float t = expf(-fabsf(a));
     return (a >= 0.0f ? 1.0f : t) / (1.0f + t);
 }
 
 __device__ __forceinline__ float silu_f(float a)
 {
+    if (a < kTailA)
+        return tail_scaled(a, a);
     float t = expf(-fabsf(a));
     return (a >= 0.0f ? a : a * t) / (1.0f + t);
+}
+
+// silu(a) * v and sigmoid(a) * v, with v taken into the product before the
+// final scaling in the tail ((a e) v: a e is 0 rather than a v overflowing).
+__device__ __forceinline__ float silu_mul_f(float a, float v)
+{
+    if (a < kTailA)
+        return ldexpf(a * expf(a + kLn2Times64) * v, -64);
+    return silu_f(a) * v;
+}
+
+__device__ __forceinline__ float sigmoid_mul_f(float a, float v)
+{
+    if (a < kTailA)
+        return tail_scaled(v, a);
+    return sigmoid_f(a) * v;
 }
 
 // The epilogue of one output: v is m_i for SILU_MUL and MUL, r_i for ADD.
@@ -49,10 +82,8 @@ __device__ __forceinline__ float apply_epilogue(int act, float a, float v)
         return sigmoid_f(a);
     case GEMV_ACT_SILU:
         return silu_f(a);
-    case GEMV_ACT_SILU_MUL: {
-        float s = silu_f(a);
-        return s * v;
-    }
+    case GEMV_ACT_SILU_MUL:
+        return silu_mul_f(a, v);
     case GEMV_ACT_MUL:
         return a * v;
     case GEMV_ACT_ADD:
@@ -402,8 +433,8 @@ __device__ __forceinline__ void lds_barrier()
 // followed by the same R up rows, and the epilogue is act(gate) * up.
 __device__ __forceinline__ float apply_glu(int act, float g, float u)
 {
-    const float a = act == GEMV_ACT_SIGMOID ? sigmoid_f(g) : silu_f(g);
-    return a * u;
+    // SILU is apply_epilogue's SILU_MUL with v = u, operation for operation
+    return act == GEMV_ACT_SIGMOID ? sigmoid_mul_f(g, u) : silu_mul_f(g, u);
 }
 
 } // namespace

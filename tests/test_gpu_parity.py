@@ -398,6 +398,55 @@ def test_epilogue_extreme_accumulators(fmt, lim):
         check_parity(w, x, act, m=m if act == "silu_mul" else None, tag=f"extreme {fmt} {act}")
 
 
+def _identity_f32(n, scale=1.0):
+    return synth.Weights("f32", n, n, (np.eye(n, dtype=np.float32) * np.float32(scale)).view(np.uint8).reshape(-1))
+
+
+def _tail_sweep(n):
+    """Accumulators through the range where e^a leaves float's normal range
+    (a < -87.3) and silu(a) itself becomes subnormal (a < -95), to -130."""
+    x = np.linspace(-130.0, 30.0, n).astype(np.float32)
+    x[:6] = [-80.5, -87.5, -95.0, -103.4375, -103.9, -108.0]
+    return x
+
+
+def test_epilogue_tail_with_large_multiplier():
+    """silu(a) * m with |m| = 40 for a in the float tail: the product is a
+    float (down to the subnormals) although e^a alone is not, and it must
+    still meet the oracle."""
+    log("epilogue tail, large multiplier")
+    N = 512
+    w = _identity_f32(N)
+    x = _tail_sweep(N)
+    m = np.full(N, 40.0, np.float32)
+    m[1::2] = -40.0
+    for act in ("silu", "sigmoid", "silu_mul"):
+        check_parity(w, x, act, m=m if act == "silu_mul" else None, tag=f"tail {act}")
+
+
+def test_glu_tail_with_large_up():
+    """The gated pair with gate sums through the float tail and up sums of
+    40 times their size (identity matrices, the up one scaled by 40), one
+    column and several; silu and sigmoid."""
+    log("gated pair tail, large up")
+    N = 512
+    wg, wu = _identity_f32(N), _identity_f32(N, 40.0)
+    x = _tail_sweep(N)
+    for act in ("silu", "sigmoid"):
+        check_glu(wg, wu, x, act, f"tail {act}")
+        X = np.stack([x, x[::-1].copy(), -x])
+        Wg, Wu, Xd = dev(wg.data), dev(wu.data), dev(X)
+        dst = torch.full((3, N), float("nan"), dtype=torch.float32, device="cuda")
+        binding.gemv_glu_ncols(Wg, Wu, "f32", N, N, 3, Xd, act, dst=dst)
+        torch.cuda.synchronize()
+        G = host(dst)
+        Y, g, gA, u, uA = oracle.glu_ncols_reference("f32", N, N, wg.data, wu.data, X, act)
+        from oracle.compare import compare_glu
+        res = compare_glu(G.reshape(-1), Y.reshape(-1), act, g.reshape(-1), gA.reshape(-1), u.reshape(-1),
+                          uA.reshape(-1))
+        assert res["max_err"] <= TOLERANCE["f32"], (act, res)
+
+
 # ------------------------------------------------------------------ gated pair (GLU)
 
 def _glu(wg, wu, x, act, out_shape=None):
