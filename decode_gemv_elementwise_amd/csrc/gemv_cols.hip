@@ -539,6 +539,21 @@ int gemv_glu_ncols(const void *W_gate, const void *W_up, int wfmt, int64_t N, in
         return st;
     if (ncols == 1)
         return gemv_glu(W_gate, W_up, wfmt, N, K, x, act, dst, hip_stream);
+    // Where one matrix's columns would run on the matrix cores, two
+    // matrix-core launches beat the vector-ALU pair (measured): the up
+    // product into dst, then the gate's with silu(g) * u in place (dst is
+    // the multiplier's identical view).  apply_epilogue's SILU_MUL and
+    // apply_glu's SILU are the same arithmetic.
+    if (GEMV_COLS_MFMA && act == GEMV_ACT_SILU && gemv::cols_mfma_plan(wfmt, (int)ncols, N, K, gemv::device_cus()).rt) {
+        const gemv::ColsCall up{static_cast<const unsigned char *>(W_up), x, (int)N, (int)K, GEMV_ACT_NONE, nullptr,
+                                nullptr, dst->data};
+        int e = gemv::launch_cols_mfma(wfmt, (int)ncols, up, hip_stream);
+        if (e != 0)
+            return gemv::finish_launch(e);
+        const gemv::ColsCall gate{static_cast<const unsigned char *>(W_gate), x, (int)N, (int)K, GEMV_ACT_SILU_MUL,
+                                  dst->data, nullptr, dst->data};
+        return gemv::finish_launch(gemv::launch_cols_mfma(wfmt, (int)ncols, gate, hip_stream));
+    }
     gemv::ColsCall c{static_cast<const unsigned char *>(W_gate), x, (int)N, (int)K, act, nullptr, nullptr,
                      dst->data, static_cast<const unsigned char *>(W_up)};
     return gemv::finish_launch(

@@ -171,15 +171,20 @@ int gemv_glu(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t 
              const gemv_view *dst, void *hip_stream);
 
 /* The gated pair over 1..8 destination columns (small-batch or speculative
- * decode), in one launch: column b of x ([ncols][K] f32) gives
+ * decode): column b of x ([ncols][K] f32) gives
  *     dst[b * N + i] = act((W_gate x_b)_i) * (W_up x_b)_i
  * with the matrices, act and alignment rules of gemv_glu; dst is an f32
- * view holding ncols * N elements that overlaps neither matrix nor x.  Both
- * matrices are read once for all columns; each chunk of a row is decoded
- * once and multiplied into every column.  Each row sum is formed exactly as
- * gemv_fused_ncols forms it on its vector-ALU column kernels, so column b
- * equals gemv_glu on x_b bit for bit (ncols == 1 is gemv_glu).  Returns
- * GEMV_OK or a negative status (GEMV_E_DIM for ncols outside 1..8);
+ * view holding ncols * N elements that overlaps neither matrix nor x.
+ * Normally one launch: both matrices are read once for all columns, each
+ * chunk of a row is decoded once and multiplied into every column, and each
+ * row sum is formed exactly as gemv_fused_ncols forms it on its vector-ALU
+ * column kernels, so column b equals gemv_glu on x_b bit for bit (ncols == 1
+ * is gemv_glu).  Where gemv_ncols_kernel reports GEMV_KERNEL_COLUMNS_MATRIX
+ * for (wfmt, N, K, ncols) and act is SILU, two matrix-core launches are
+ * faster and are taken instead: the up product into dst, then the gate's
+ * with silu(g) * u in place; the results then carry the matrix-core
+ * kernel's precision (within the formats' tolerances, not bit for bit).
+ * Returns GEMV_OK or a negative status (GEMV_E_DIM for ncols outside 1..8);
  * asynchronous on hip_stream; allocates nothing. */
 int gemv_glu_ncols(const void *W_gate, const void *W_up, int wfmt, int64_t N, int64_t K, int64_t ncols,
                    const float *x, int act, const gemv_view *dst, void *hip_stream);

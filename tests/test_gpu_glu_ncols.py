@@ -64,9 +64,34 @@ def test_glu_ncols_columns_equal_one_column_pair_bitwise(fmt, N, K, B):
     wg = synth.random_weights(rng, fmt, N, K)
     wu = synth.random_weights(rng, fmt, N, K)
     X = np.stack([synth.draw_vec(rng, K) for _ in range(B)])
-    G = _run(wg, wu, X, "silu")
-    for b in range(B):
-        assert np.array_equal(G[b].view(np.uint32), _one(wg, wu, X[b], "silu").view(np.uint32)), (fmt, b)
+    # sigmoid always takes the one-launch pair; silu too unless the matrix
+    # cores take the columns (then two matrix-core launches, not bitwise)
+    acts = ["sigmoid"] + (["silu"] if binding.gemv_ncols_kernel(fmt, N, K, B) != "columns_matrix" else [])
+    for act in acts:
+        G = _run(wg, wu, X, act)
+        for b in range(B):
+            assert np.array_equal(G[b].view(np.uint32), _one(wg, wu, X[b], act).view(np.uint32)), (fmt, act, b)
+
+
+@pytest.mark.parametrize("fmt,N,K,B", [("q4b32", 14336, 4096, 4), ("q4b32", 4096, 4096, 8), ("q8b32", 14336, 4096, 8)])
+def test_glu_ncols_matrix_core_route(fmt, N, K, B):
+    """Where the columns run on the matrix cores, silu pairs take two
+    matrix-core launches (up into dst, gate with silu * up in place); the
+    result still meets the oracle, and equals that composition by hand."""
+    assert binding.gemv_ncols_kernel(fmt, N, K, B) == "columns_matrix"
+    rng = np.random.default_rng(zlib.crc32(f"glumfma/{fmt}/{N}/{K}/{B}".encode()))
+    wg = synth.random_weights(rng, fmt, N, K)
+    wu = synth.random_weights(rng, fmt, N, K)
+    X = np.stack([synth.draw_vec(rng, K) for _ in range(B)])
+    G = _check(wg, wu, X, "silu", f"{fmt} {N}x{K} {B} matrix-core route")
+    Wg, Wu, Xd = dev(wg.data), dev(wu.data), dev(X)
+    up = torch.empty(B, N, dtype=torch.float32, device="cuda")
+    out = torch.empty(B, N, dtype=torch.float32, device="cuda")
+    binding.gemv_fused_ncols(Wu, fmt, N, K, B, Xd, "none", dst=up)
+    binding.gemv_fused_ncols(Wg, fmt, N, K, B, Xd, "silu_mul", mul_operand=up, dst=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.view(np.uint32), host(out).view(np.uint32))
+    _check(wg, wu, X, "sigmoid", f"{fmt} {N}x{K} {B} sigmoid, one launch")
 
 
 @pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])

@@ -87,6 +87,19 @@ def test_graph_ncols(fmt, N, K, B, act):
     _replays_match(f"ncols {fmt} {B}", lambda d: binding.gemv_fused_ncols(Wd, fmt, N, K, B, X, act, dst=d, **kw), out)
 
 
+@pytest.mark.parametrize("fmt,B", [("f16", 4), ("q4b32", 4)])
+def test_graph_glu_ncols(fmt, B):
+    log(f"graph gemv_glu_ncols {fmt} ncols={B}")
+    rng = np.random.default_rng(44)
+    N, K = 14336, 4096
+    wg = synth.random_weights(rng, fmt, N, K)
+    wu = synth.random_weights(rng, fmt, N, K)
+    Wg, Wu = dev(wg.data), dev(wu.data)
+    X = dev(np.stack([synth.draw_vec(rng, K) for _ in range(B)]))
+    out = torch.empty(B, N, dtype=torch.float32, device="cuda")
+    _replays_match(f"glu ncols {fmt}", lambda d: binding.gemv_glu_ncols(Wg, Wu, fmt, N, K, B, X, "silu", dst=d), out)
+
+
 def test_graph_hadamard():
     log("graph gemv_fwht_signed, gemv_fused_fwht")
     rng = np.random.default_rng(43)
