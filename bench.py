@@ -125,7 +125,7 @@ class Step:
                         for c in self.calls}
         self.tmp_buf = {c.name: torch.zeros((R, c.ncols * wl.weights[c.w].N), dtype=torch.float32, device=dev)
                         for c in self.calls}
-        self.up_buf = {c.name: torch.zeros((R, wl.weights[c.w].N), dtype=torch.float32, device=dev)
+        self.up_buf = {c.name: torch.zeros((R, c.ncols * wl.weights[c.w].N), dtype=torch.float32, device=dev)
                        for c in self.calls if c.w2}
         self.xt_buf = {c.name: torch.zeros((R, wl.weights[c.w].K), dtype=torch.float32, device=dev)
                        for c in self.calls if c.fwht}
@@ -156,7 +156,16 @@ class Step:
                 dst = r if c.act == "add" else m
             else:
                 dst = self.out_buf[c.name][i].view(shape)
-            if c.w2:
+            if c.w2 and c.ncols > 1:
+                W2 = self.w_buf[c.w2][i * self.w_slot[c.w2]:]
+                if unfused:  # up (none), gate (none) over the columns, then silu(gate) * up
+                    up, tmp = self.up_buf[c.name][i].view(shape), self.tmp_buf[c.name][i].view(shape)
+                    fns.append(binding.PreparedNcols(W2, w.fmt, w.N, w.K, c.ncols, x, "none", dst=up))
+                    fns.append(binding.PreparedNcols(W, w.fmt, w.N, w.K, c.ncols, x, "none", dst=tmp))
+                    fns.append(_PreparedEpilogue(binding, "silu_mul", c.ncols * w.N, tmp, up, None, dst))
+                else:
+                    fns.append(binding.PreparedGluNcols(W, W2, w.fmt, w.N, w.K, c.ncols, x, c.act, dst=dst))
+            elif c.w2:
                 W2 = self.w_buf[c.w2][i * self.w_slot[c.w2]:]
                 if unfused:  # up (none), gate (none), then silu(gate) * up
                     up, tmp = self.up_buf[c.name][i], self.tmp_buf[c.name][i]
@@ -338,7 +347,10 @@ def cpu_baseline(wl, seconds):
             x = outputs[c.x[1:]] if c.x.startswith("@") else wl.vectors[c.x]
             m = (outputs[c.m[1:]] if c.m.startswith("@") else wl.vectors[c.m]) if c.m else None
             r = wl.vectors[c.r] if c.r else None
-            if c.w2:
+            if c.w2 and c.ncols > 1:
+                y = oracle.glu_ncols_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data,
+                                               np.reshape(x, (c.ncols, w.K)), c.act)[0].reshape(-1)
+            elif c.w2:
                 y = oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act)[0]
             elif c.fwht:
                 y = oracle.fwht_gemv_reference(w.fmt, w.N, w.K, w.data, x, wl.vectors[c.fwht[0]], c.fwht[1], c.act,
@@ -460,7 +472,11 @@ def bench_workload(torch, binding, synth, name, args, probe):
     dom_flops = 2 * dom_w.N * dom_w.K * dom.ncols * (2 if dom.w2 else 1)
     achieved = dom_bytes / dom_sec / 1e9
     cols_kernel = binding.gemv_ncols_kernel(dom_w.fmt, dom_w.N, dom_w.K, dom.ncols) if dom.ncols > 1 else None
-    if cols_kernel == "columns_matrix":
+    if dom.w2 and dom.ncols > 1:
+        kernel_name = (f"gemv_cols_mfma_kernel<{dom_w.fmt}, ncols={dom.ncols}> x2, gated pair as up then gate ({dom.name})"
+                       if cols_kernel == "columns_matrix" and dom.act == "silu" else
+                       f"gemv_cols_kernel<{dom_w.fmt}, ncols={dom.ncols}, gated pair> ({dom.name})")
+    elif cols_kernel == "columns_matrix":
         kernel_name = f"gemv_cols_mfma_kernel<{dom_w.fmt}, ncols={dom.ncols}> ({dom.name})"
     elif dom.ncols > 1:
         kernel_name = f"gemv_cols_kernel<{dom_w.fmt}, ncols={dom.ncols}> ({dom.name})"

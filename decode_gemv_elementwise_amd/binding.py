@@ -308,6 +308,21 @@ class PreparedGlu:
             _raise(st)
 
 
+class PreparedGluNcols:
+    """A gemv_glu_ncols call with its dst view marshalled once."""
+
+    def __init__(self, W_gate, W_up, wfmt, N, K, ncols, x, act="silu", dst=None):
+        self._lib = load()
+        self._view = make_view(dst)
+        self._ptr = ctypes.pointer(self._view)
+        self._args = (_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, ncols, _addr(x), _act(act))
+
+    def __call__(self, stream=None):
+        st = self._lib.gemv_glu_ncols(*self._args, self._ptr, _stream(stream))
+        if st != 0:
+            _raise(st)
+
+
 class PreparedCall:
     """A gemv_fused call with its views marshalled once, for tight loops and
     graph capture (the tensors must stay alive and in place)."""

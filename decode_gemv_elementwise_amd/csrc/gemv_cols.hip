@@ -274,18 +274,21 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void g
             break;
     }
 
-    // 5. reduce every (row, column) sum; lane j takes output j
-    float mine = 0.0f;
+    // 5. reduce every (row, column) sum; lane j takes output j (and its up
+    //    sum for a gated pair), then one epilogue per lane
+    float mine = 0.0f, mine2 = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float sum = wave_sum(acc[r][c]);
-            if constexpr (GLU)
-                sum = apply_glu(act, sum, wave_sum(acc[R + r][c]));
+            const float sum = wave_sum(acc[r][c]);
             mine = lane == c * R + r ? sum : mine;
+            if constexpr (GLU) {
+                const float sum2 = wave_sum(acc[R + r][c]);
+                mine2 = lane == c * R + r ? sum2 : mine2;
+            }
         }
-    const float y = GLU ? mine : apply_epilogue(act, mine, opv);
+    const float y = GLU ? apply_glu(act, mine, mine2) : apply_epilogue(act, mine, opv);
     if (lane < R * NC && row0 + lane % R < N)
         dst[(int64_t)(lane / R) * N + row0 + lane % R] = y;
 }
@@ -341,18 +344,20 @@ __global__ __launch_bounds__(256) void gemv_cols_generic_kernel(const unsigned c
                     acc2[c] = fmaf(w2, x[(int64_t)c * K + k], acc2[c]);
             }
         }
-        float mine = 0.0f;
+        float mine = 0.0f, mine2 = 0.0f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            float sum = wave_sum(acc[c]);
-            if constexpr (GLU)
-                sum = apply_glu(act, sum, wave_sum(acc2[c]));
+            const float sum = wave_sum(acc[c]);
             mine = lane == c ? sum : mine;
+            if constexpr (GLU) {
+                const float sum2 = wave_sum(acc2[c]);
+                mine2 = lane == c ? sum2 : mine2;
+            }
         }
         if (lane < NC) {
             const int64_t o = (int64_t)lane * N + row;
             if constexpr (GLU) {
-                dst[o] = mine;
+                dst[o] = apply_glu(act, mine, mine2);
             } else {
                 const bool has_op = act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL || act == GEMV_ACT_ADD;
                 const float v = has_op ? (act == GEMV_ACT_ADD ? rop[o] : mop[o]) : 0.0f;

@@ -278,6 +278,18 @@ def q4b32_gate_14336x4096_ncols4(seed: int = 0) -> Workload:
                     "4-bit 14336x4096 silu over four columns")
 
 
+def bf16_swiglu_14336x4096_ncols4(seed: int = 0) -> Workload:
+    """The bf16 gate and up projections of a 4096-hidden, 14336-FFN layer as
+    one gated pair over four destination columns (small-batch decode)."""
+    rng = np.random.default_rng(seed)
+    Wg = draw_float_weights(rng, "bf16", 14336, 4096, 1.0 / 4096)
+    Wu = draw_float_weights(rng, "bf16", 14336, 4096, 1.0 / 4096)
+    x = draw_vec(rng, 4 * 4096)
+    calls = [Call("bf16_gate_up_glu_ncols4", "Wgate", "x", "silu", w2="Wup", ncols=4)]
+    return Workload("bf16_swiglu_14336x4096_ncols4", {"Wgate": Wg, "Wup": Wu}, {"x": x}, calls,
+                    "bf16 14336x4096 gate and up, silu(W_g x_b) * (W_u x_b) over four columns")
+
+
 WORKLOADS = {
     "f32_tiny_256": f32_tiny_256,
     "f16_outproj_residual_4096": f16_outproj_residual_4096,
@@ -288,6 +300,7 @@ WORKLOADS = {
     "f16_outproj_residual_4096_ncols8": f16_outproj_residual_4096_ncols8,
     "f16_outproj_fwht_residual_4096": f16_outproj_fwht_residual_4096,
     "q4b32_gate_14336x4096_ncols4": q4b32_gate_14336x4096_ncols4,
+    "bf16_swiglu_14336x4096_ncols4": bf16_swiglu_14336x4096_ncols4,
 }
 
 

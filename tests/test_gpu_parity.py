@@ -47,7 +47,12 @@ def test_workload_calls_full_size(wname):
         x = _resolve(wl, c.x, outputs)
         m = _resolve(wl, c.m, outputs)
         r = _resolve(wl, c.r, outputs)
-        if c.w2:
+        if c.w2 and c.ncols > 1:
+            from test_gpu_glu_ncols import _check as check_glu_ncols
+            X = np.reshape(x, (c.ncols, w.K))
+            check_glu_ncols(w, wl.weights[c.w2], X, c.act, f"{wname}/{c.name}")
+            y = oracle.glu_ncols_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, X, c.act)[0].reshape(-1)
+        elif c.w2:
             check_glu(w, wl.weights[c.w2], x, c.act, f"{wname}/{c.name}")
             y = oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act)[0]
         elif c.fwht:
