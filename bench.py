@@ -475,7 +475,7 @@ def bench_workload(torch, binding, synth, name, args, probe):
     if dom.w2 and dom.ncols > 1:
         kernel_name = (f"gemv_cols_mfma_kernel<{dom_w.fmt}, ncols={dom.ncols}> x2, gated pair as up then gate ({dom.name})"
                        if cols_kernel == "columns_matrix" and dom.act == "silu" else
-                       f"gemv_cols_kernel<{dom_w.fmt}, ncols={dom.ncols}, gated pair> ({dom.name})")
+                       f"gemv_cols(_tiles)_kernel<{dom_w.fmt}, ncols={dom.ncols}, gated pair> ({dom.name})")
     elif cols_kernel == "columns_matrix":
         kernel_name = f"gemv_cols_mfma_kernel<{dom_w.fmt}, ncols={dom.ncols}> ({dom.name})"
     elif dom.ncols > 1:

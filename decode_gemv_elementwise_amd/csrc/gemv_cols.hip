@@ -27,6 +27,9 @@
 //    16) consecutive lanes fall in distinct bank groups.
 //  * Lane j < R * ncols finishes output (row R-block j % R, column j / R):
 //    consecutive lanes store consecutive rows of one column.
+//  * The gated pair's one-shot form runs on a resident grid
+//    (gemv_cols_tiles_kernel): a workgroup stages x once and walks row tiles,
+//    so no tile waits for a fresh copy of x before issuing its W.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -55,6 +58,31 @@ namespace {
 #ifndef GEMV_COLS_ONESHOT
 #define GEMV_COLS_ONESHOT 1
 #endif
+// one-shot shape: waves per workgroup and output rows per wave, for plain
+// columns and for the gated pair (which loads two rows per output row)
+#ifndef GEMV_COLS_OS_WAVES
+#define GEMV_COLS_OS_WAVES 8
+#endif
+#ifndef GEMV_COLS_OS_R
+#define GEMV_COLS_OS_R 2
+#endif
+#ifndef GEMV_COLS_OS_GLU_WAVES
+#define GEMV_COLS_OS_GLU_WAVES 8
+#endif
+#ifndef GEMV_COLS_OS_GLU_R
+#define GEMV_COLS_OS_GLU_R 1
+#endif
+// one-shot grid, for plain columns and for the gated pair: 0 one workgroup
+// per row tile; 1 a resident grid walking the tiles; 2 the same with the
+// tiles spread evenly over the workgroups.  Measured (14336x4096, graph
+// replay): the resident grid takes 2-9 % off the gated pair (8-bit at 4
+// columns 33.6 -> 30.6 us) and changes plain columns by +-1 %.
+#ifndef GEMV_COLS_OS_PERSIST
+#define GEMV_COLS_OS_PERSIST 0
+#endif
+#ifndef GEMV_COLS_OS_PERSIST_GLU
+#define GEMV_COLS_OS_PERSIST_GLU 1
+#endif
 // f16 and the block formats take the matrix-core kernel (gemv_mfma.hip)
 // where the shape fits it
 #ifndef GEMV_COLS_MFMA
@@ -68,7 +96,7 @@ namespace {
 // 2 * UO loads per lane in flight.
 template <int FMT, int NC, int UO = 0, bool GLU = false> struct ColsCfg {
     static constexpr int E = Fmt<FMT>::E;
-    static constexpr int kWaves = UO > 0 ? 8 : GEMV_COLS_WAVES;
+    static constexpr int kWaves = UO > 0 ? (GLU ? GEMV_COLS_OS_GLU_WAVES : GEMV_COLS_OS_WAVES) : GEMV_COLS_WAVES;
     // chunks per lane per segment: GEMV_COLS_X_BUDGET / (NC * E), 1..8 (a
     // short segment keeps the LDS per workgroup small and occupancy up)
     static constexpr int kU0 = GEMV_COLS_X_BUDGET / (NC * E);
@@ -76,13 +104,15 @@ template <int FMT, int NC, int UO = 0, bool GLU = false> struct ColsCfg {
     // rows per wave: about GEMV_COLS_LOADS chunk loads per lane per batch, 1..4
     // (a gated pair loads a gate and an up row per output row: half as many)
     static constexpr int kR0 = GEMV_COLS_LOADS / U;
-    static constexpr int kR1 = UO > 0 ? 2 : (kR0 > 4 ? 4 : (kR0 < 1 ? 1 : kR0));
-    static constexpr int R = GLU ? (kR1 > 1 ? kR1 / 2 : 1) : kR1;
+    static constexpr int kR1 = UO > 0 ? GEMV_COLS_OS_R : (kR0 > 4 ? 4 : (kR0 < 1 ? 1 : kR0));
+    static constexpr int R = GLU ? (UO > 0 ? GEMV_COLS_OS_GLU_R : (kR1 > 1 ? kR1 / 2 : 1)) : kR1;
     static constexpr int SEG = 64 * U * E;     // x floats per column per segment
     static constexpr int kPlane4 = SEG / 4;    // float4 slots per plane (a multiple of 64)
     static constexpr int kBuf4 = NC * kPlane4; // float4 slots per segment buffer
     static constexpr int kCopies = kBuf4 / kWave;                // 64-slot wave copies per segment
     static constexpr int kDma = (kCopies + kWaves - 1) / kWaves; // copies per wave (the last may be idle)
+    static_assert(R * NC <= kWave, "a wave's outputs are finished one per lane");
+    static_assert(kWaves * kWave <= 1024, "at most 1024 threads per workgroup");
 };
 
 // Copies segment seg of x (all columns) from global memory straight into an
@@ -92,11 +122,11 @@ template <int FMT, int NC, int UO = 0, bool GLU = false> struct ColsCfg {
 // 16-byte aligned the same slots are filled by 4-byte copies, 16 slots per
 // instruction.  Elements past K fetch a clamped, valid address; those slots
 // belong to chunks past the end of the row and are never used.
-template <int FMT, int NC, int UO>
+template <int FMT, int NC, int UO, bool GLU>
 __device__ __forceinline__ void dma_x_segment(f32x4 *buf, const float *x, int K, int seg, int wave, int lane,
                                               bool aligned16)
 {
-    using C = ColsCfg<FMT, NC, UO>;
+    using C = ColsCfg<FMT, NC, UO, GLU>; // the kernel's own wave count splits the copies
     const int k4 = K / 4; // K is a multiple of 4 on this path
     if (aligned16) {
 #pragma unroll
@@ -212,7 +242,7 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void g
 
     // 2. x of the first segment, straight into LDS
     const bool x16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-    dma_x_segment<FMT, NC, UO>(xa, x, K, 0, wave, lane, x16);
+    dma_x_segment<FMT, NC, UO, GLU>(xa, x, K, 0, wave, lane, x16);
 
     // 3. W, first batch
     const unsigned char *wrow[RR];
@@ -257,7 +287,7 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void g
         __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0); expcnt, lgkmcnt not waited for
         __builtin_amdgcn_s_barrier();
         if (s + 1 < nseg) {
-            dma_x_segment<FMT, NC, UO>(xb, x, K, s + 1, wave, lane, x16);
+            dma_x_segment<FMT, NC, UO, GLU>(xb, x, K, s + 1, wave, lane, x16);
             issue_batch<FMT, RR, U>(b1, wrow, srow, lane, (s + 1) * U, nchunks);
         }
         consume_cols<FMT, NC, UO, RR, U>(b0, xa, acc, lane, s * SEGC, nchunks);
@@ -266,7 +296,7 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void g
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __builtin_amdgcn_s_barrier();
         if (s + 1 < nseg) {
-            dma_x_segment<FMT, NC, UO>(xa, x, K, s + 1, wave, lane, x16);
+            dma_x_segment<FMT, NC, UO, GLU>(xa, x, K, s + 1, wave, lane, x16);
             issue_batch<FMT, RR, U>(b0, wrow, srow, lane, (s + 1) * U, nchunks);
         }
         consume_cols<FMT, NC, UO, RR, U>(b1, xb, acc, lane, s * SEGC, nchunks);
@@ -291,6 +321,87 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void g
     const float y = GLU ? apply_glu(act, mine, mine2) : apply_epilogue(act, mine, opv);
     if (lane < R * NC && row0 + lane % R < N)
         dst[(int64_t)(lane / R) * N + row0 + lane % R] = y;
+}
+
+// The one-shot form on a resident grid: each workgroup stages x of every
+// column once, then walks the row tiles blockIdx.x, blockIdx.x + gridDim.x,
+// ...; a tile's rows are computed exactly as in gemv_cols_kernel (same lanes,
+// same chunk order, same reduction), so results are bitwise the same.  Tiles
+// after the first need no barrier: x in LDS is only read.
+template <int FMT, int NC, int UO, bool GLU>
+__global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void gemv_cols_tiles_kernel(
+    const unsigned char *__restrict__ W, const float *__restrict__ x, int N, int K, int act, const float *mop,
+    const float *rop, float *dst, const unsigned char *__restrict__ W2)
+{
+    static_assert(UO > 0, "the whole row is one segment");
+    using F = Fmt<FMT>;
+    using C = ColsCfg<FMT, NC, UO, GLU>;
+    constexpr int R = C::R, U = C::U;
+    constexpr int RR = GLU ? 2 * R : R;
+    extern __shared__ f32x4 lds4[];
+    f32x4 *const xa = lds4;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nchunks = K / F::E;
+    const int ntiles = (N + C::kWaves * R - 1) / (C::kWaves * R);
+    const int64_t rbytes = row_bytes<FMT>(K);
+    const unsigned char *scales = F::kBlock ? W + align256_dev((int64_t)N * rbytes) : nullptr;
+    const unsigned char *scales2 = (F::kBlock && GLU) ? W2 + align256_dev((int64_t)N * rbytes) : nullptr;
+    const int64_t sbytes = (int64_t)(K / 32) * 2;
+    const int jo = min(lane, R * NC - 1);
+    const bool has_op = act == GEMV_ACT_SILU_MUL || act == GEMV_ACT_MUL || act == GEMV_ACT_ADD;
+    const float *opp = act == GEMV_ACT_ADD ? rop : (has_op ? mop : x);
+
+    const bool x16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    dma_x_segment<FMT, NC, UO, GLU>(xa, x, K, 0, wave, lane, x16);
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0); expcnt, lgkmcnt not waited for
+    __builtin_amdgcn_s_barrier();
+
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int row0 = (tile * C::kWaves + wave) * R;
+        // epilogue operand first: the loads retire in order, so the W waits
+        // below cover it
+        const int orow = min(row0 + jo % R, N - 1), ocol = jo / R;
+        const float opv = opp[has_op ? (int64_t)ocol * N + orow : 0];
+        const unsigned char *wrow[RR];
+        const unsigned char *srow[RR];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = min(row0 + r, N - 1);
+            wrow[r] = W + (int64_t)row * rbytes;
+            srow[r] = F::kBlock ? scales + (int64_t)row * sbytes : nullptr;
+            if constexpr (GLU) {
+                wrow[R + r] = W2 + (int64_t)row * rbytes;
+                srow[R + r] = F::kBlock ? scales2 + (int64_t)row * sbytes : nullptr;
+            }
+        }
+        Batch<FMT, RR, U> b0;
+        issue_batch<FMT, RR, U>(b0, wrow, srow, lane, 0, nchunks);
+        float acc[RR][NC];
+#pragma unroll
+        for (int r = 0; r < RR; ++r)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                acc[r][c] = 0.0f;
+        consume_cols<FMT, NC, UO, RR, U>(b0, xa, acc, lane, 0, nchunks);
+
+        float mine = 0.0f, mine2 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float sum = wave_sum(acc[r][c]);
+                mine = lane == c * R + r ? sum : mine;
+                if constexpr (GLU) {
+                    const float sum2 = wave_sum(acc[R + r][c]);
+                    mine2 = lane == c * R + r ? sum2 : mine2;
+                }
+            }
+        const float y = GLU ? apply_glu(act, mine, mine2) : apply_epilogue(act, mine, opv);
+        if (lane < R * NC && row0 + lane % R < N)
+            dst[(int64_t)(lane / R) * N + row0 + lane % R] = y;
+    }
 }
 
 // Any K (float formats whose rows are not whole 16-byte chunks, or x too long
@@ -386,7 +497,32 @@ template <int FMT, int NC, int UO, bool GLU = false> hipError_t launch_cols(cons
             return attr_err;
     }
     const int rows_per_tile = C::kWaves * C::R;
-    const int grid = (c.N + rows_per_tile - 1) / rows_per_tile;
+    int grid = (c.N + rows_per_tile - 1) / rows_per_tile;
+    constexpr int kPersist = GLU ? GEMV_COLS_OS_PERSIST_GLU : GEMV_COLS_OS_PERSIST;
+    if constexpr (UO > 0 && kPersist > 0) {
+        fn = reinterpret_cast<const void *>(&gemv_cols_tiles_kernel<FMT, NC, UO, GLU>);
+        static std::once_flag once;
+        static hipError_t attr_err = hipSuccess;
+        static int per_cu = 0;
+        constexpr size_t lds1 = (size_t)C::kBuf4 * 16; // one segment: lds == lds1 here
+        std::call_once(once, [&] {
+            if (lds1 > 64 * 1024)
+                attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+            if (attr_err == hipSuccess)
+                attr_err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, C::kWaves * kWave, lds1);
+        });
+        if (attr_err != hipSuccess)
+            return attr_err;
+        const int slots = (per_cu > 0 ? per_cu : 1) * device_cus();
+        if (grid > slots) {
+            if (kPersist == 2) {
+                const int per_wg = (grid + slots - 1) / slots;
+                grid = (grid + per_wg - 1) / per_wg;
+            } else {
+                grid = slots;
+            }
+        }
+    }
     const unsigned char *W = c.W;
     const float *x = c.x;
     int N = c.N, K = c.K, act = c.act;
