@@ -106,6 +106,23 @@ def test_glu_ncols_odd_k_generic_path(fmt):
         assert np.array_equal(G[b].view(np.uint32), _one(wg, wu, X[b], "silu").view(np.uint32)), (fmt, b)
 
 
+@pytest.mark.parametrize("fmt,N,K,B", [("bf16", 8 * 600 + 5, 4096, 4), ("q8b32", 8 * 700 + 3, 4096, 2),
+                                       ("q4b32", 8 * 700 + 3, 4096, 2)])
+def test_glu_ncols_resident_grid_walks_ragged_tiles(fmt, N, K, B):
+    """Shapes with more 8-row tiles than resident workgroups and a ragged last
+    tile: the one-shot pair's workgroups walk several tiles each, and every
+    column must still match the oracle and the one-column pair bit for bit."""
+    assert binding.gemv_ncols_kernel(fmt, N, K, B) == "columns"
+    rng = np.random.default_rng(zlib.crc32(f"gluresident/{fmt}/{N}/{K}/{B}".encode()))
+    wg = synth.random_weights(rng, fmt, N, K)
+    wu = synth.random_weights(rng, fmt, N, K)
+    X = np.stack([synth.draw_vec(rng, K) for _ in range(B)])
+    for act in ("silu", "sigmoid"):
+        G = _check(wg, wu, X, act, f"resident grid {fmt} {N}x{K} {B} {act}")
+        for b in range(B):
+            assert np.array_equal(G[b].view(np.uint32), _one(wg, wu, X[b], act).view(np.uint32)), (fmt, act, b)
+
+
 def test_glu_ncols_full_size_gate_up():
     """The 4-bit gate and up projections of the decode layer, 4 columns."""
     rng = np.random.default_rng(72)
