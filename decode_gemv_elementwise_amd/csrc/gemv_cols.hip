@@ -27,9 +27,9 @@
 //    16) consecutive lanes fall in distinct bank groups.
 //  * Lane j < R * ncols finishes output (row R-block j % R, column j / R):
 //    consecutive lanes store consecutive rows of one column.
-//  * The gated pair's one-shot form runs on a resident grid
-//    (gemv_cols_tiles_kernel): a workgroup stages x once and walks row tiles,
-//    so no tile waits for a fresh copy of x before issuing its W.
+//  * The one-shot form runs on a resident grid (gemv_cols_tiles_kernel): a
+//    workgroup stages x once and walks row tiles, so no tile waits for a
+//    fresh copy of x before issuing its W.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -74,11 +74,12 @@ namespace {
 #endif
 // one-shot grid, for plain columns and for the gated pair: 0 one workgroup
 // per row tile; 1 a resident grid walking the tiles; 2 the same with the
-// tiles spread evenly over the workgroups.  Measured (14336x4096, graph
-// replay): the resident grid takes 2-9 % off the gated pair (8-bit at 4
-// columns 33.6 -> 30.6 us) and changes plain columns by +-1 %.
+// tiles spread evenly over the workgroups.  Measured (graph replay): the
+// resident grid takes 2-9 % off the gated pair at 14336x4096 (8-bit at 4
+// columns 33.6 -> 30.6 us) and 0-3 % off float-format plain columns
+// (within +-1 % for the block formats).
 #ifndef GEMV_COLS_OS_PERSIST
-#define GEMV_COLS_OS_PERSIST 0
+#define GEMV_COLS_OS_PERSIST 1
 #endif
 #ifndef GEMV_COLS_OS_PERSIST_GLU
 #define GEMV_COLS_OS_PERSIST_GLU 1
@@ -568,17 +569,15 @@ template <int FMT, int NC, bool GLU = false> hipError_t dispatch_cols(const Cols
     constexpr int UO = oneshot_u<FMT>();
     const int cpl = (c.K / Fmt<FMT>::E + kWave - 1) / kWave;
     if constexpr (NC * kWave * UO * Fmt<FMT>::E * 4 <= kMaxLds) {
-        // measured: the block formats gain wherever it fits; the float
-        // formats from 3 columns, while every CU gets a 16-row workgroup and
-        // either x of all columns stays within 64 KiB (two workgroups per CU)
-        // or the workgroups are one round (one per CU).  The gated pair, on
-        // its resident grid, gains wherever x stays within 64 KiB, at any
-        // row count (f32 4096x2048 at 2 columns 14.7 -> 12.2 us, bf16
-        // 2048x4096 at 4 columns 11.1 -> 9.3 us) and loses ~1 % beyond it.
+        // measured on the resident grid: the block formats gain wherever it
+        // fits; the float formats wherever x of all columns stays within
+        // 64 KiB (two workgroups per CU), at any row count (bf16 1024x4096
+        // at 3 columns 7.5 -> 6.2 us, f16 4096^2 at 2 columns 8.6 -> 8.0 us;
+        // the gated pair: f32 4096x2048 at 2 columns 14.7 -> 12.2 us), and
+        // beyond it only where the 16-row workgroups are exactly one round
         const int64_t lds = (int64_t)NC * kWave * cpl * Fmt<FMT>::E * 4;
         const int64_t wgs = (c.N + 15) / 16, cus = device_cus();
-        const bool take = Fmt<FMT>::kBlock || (GLU && lds <= 64 * 1024) ||
-                          (NC >= 3 && wgs >= cus && (lds <= 64 * 1024 || wgs <= cus));
+        const bool take = Fmt<FMT>::kBlock || lds <= 64 * 1024 || (NC >= 3 && wgs == cus);
         if (GEMV_COLS_ONESHOT && cpl <= UO && take)
             return launch_cols<FMT, NC, UO, GLU>(c, s);
     }
