@@ -135,6 +135,27 @@ def test_ncols_inplace_and_view():
     check_ncols(w, X, "silu_mul", M=M, inplace=True, tag="silu_mul in place")
 
 
+@pytest.mark.parametrize("fmt,N,K,act", [("bf16", 16 * 600 + 7, 4096, "add"), ("f16", 16 * 600 + 7, 4096, "silu_mul"),
+                                         ("f32", 16 * 600 + 7, 2048, "sigmoid"), ("q8b32", 16 * 700 + 9, 4096, "mul"),
+                                         ("q4b32", 16 * 700 + 9, 4096, "silu")])
+def test_ncols_resident_grid_walks_ragged_tiles(fmt, N, K, act):
+    """Two columns with more 16-row tiles than resident workgroups and a
+    ragged last tile: the one-shot form's workgroups walk several tiles
+    each; every column must match the oracle and the one-column call bit
+    for bit."""
+    B = 2
+    assert binding.gemv_ncols_kernel(fmt, N, K, B) == "columns"
+    rng = np.random.default_rng(zlib.crc32(f"ncolsresident/{fmt}/{N}/{K}".encode()))
+    w = synth.random_weights(rng, fmt, N, K)
+    X = rng.normal(size=(B, K)).astype(np.float32)
+    M, R = _operands(rng, act, B, N)
+    log(f"ncols resident grid fmt={fmt} N={N} K={K} act={act}")
+    g = check_ncols(w, X, act, M, R, tag="resident grid").reshape(B, N)
+    for b in range(B):
+        one = _one_column(w, X[b], act, None if M is None else M[b], None if R is None else R[b])
+        assert np.array_equal(g[b].view(np.uint32), one.view(np.uint32)), (fmt, b)
+
+
 @pytest.mark.parametrize("fmt,N,K,act", [("q4b32", 14336, 4096, "silu"), ("bf16", 14336, 4096, "silu_mul"),
                                          ("f16", 4096, 4096, "add"), ("q4b32", 4096, 14336, "add"),
                                          ("q8b32", 14336, 4096, "mul"), ("q8b32", 4096, 6144, "silu"),
