@@ -359,14 +359,7 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void g
     __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0); expcnt, lgkmcnt not waited for
     __builtin_amdgcn_s_barrier();
 
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int row0 = (tile * C::kWaves + wave) * R;
-        // epilogue operand first: the loads retire in order, so the W waits
-        // below cover it
-        const int orow = min(row0 + jo % R, N - 1), ocol = jo / R;
-        const float opv = opp[has_op ? (int64_t)ocol * N + orow : 0];
-        const unsigned char *wrow[RR];
-        const unsigned char *srow[RR];
+    auto tile_rows = [&](int row0, const unsigned char *(&wrow)[RR], const unsigned char *(&srow)[RR]) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = min(row0 + r, N - 1);
@@ -377,16 +370,20 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void g
                 srow[R + r] = F::kBlock ? scales2 + (int64_t)row * sbytes : nullptr;
             }
         }
-        Batch<FMT, RR, U> b0;
-        issue_batch<FMT, RR, U>(b0, wrow, srow, lane, 0, nchunks);
+    };
+    auto operand_of = [&](int row0) {
+        const int orow = min(row0 + jo % R, N - 1), ocol = jo / R;
+        return opp[has_op ? (int64_t)ocol * N + orow : 0];
+    };
+    // consume a landed batch, reduce every (row, column) sum and store
+    auto finish = [&](const Batch<FMT, RR, U> &b, int row0, float opv) {
         float acc[RR][NC];
 #pragma unroll
         for (int r = 0; r < RR; ++r)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
                 acc[r][c] = 0.0f;
-        consume_cols<FMT, NC, UO, RR, U>(b0, xa, acc, lane, 0, nchunks);
-
+        consume_cols<FMT, NC, UO, RR, U>(b, xa, acc, lane, 0, nchunks);
         float mine = 0.0f, mine2 = 0.0f;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -402,6 +399,19 @@ __global__ __launch_bounds__((ColsCfg<FMT, NC, UO, GLU>::kWaves * kWave)) void g
         const float y = GLU ? apply_glu(act, mine, mine2) : apply_epilogue(act, mine, opv);
         if (lane < R * NC && row0 + lane % R < N)
             dst[(int64_t)(lane / R) * N + row0 + lane % R] = y;
+    };
+    const unsigned char *wrow[RR];
+    const unsigned char *srow[RR];
+
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int row0 = (tile * C::kWaves + wave) * R;
+        // epilogue operand first: the loads retire in order, so the W waits
+        // below cover it
+        const float opv = operand_of(row0);
+        tile_rows(row0, wrow, srow);
+        Batch<FMT, RR, U> b0;
+        issue_batch<FMT, RR, U>(b0, wrow, srow, lane, 0, nchunks);
+        finish(b0, row0, opv);
     }
 }
 
