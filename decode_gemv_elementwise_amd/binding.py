@@ -148,6 +148,87 @@ def _as_view(v):
     return ctypes.pointer(make_view(v))
 
 
+# ------------------------------------------------------------------ tensor checks of the launching calls
+# A launch hands raw addresses to kernels, so a host tensor, a tensor on
+# another device, a wrong dtype or a buffer shorter than what the kernel reads
+# would become an out-of-bounds or host-address access on the GPU.  Every torch
+# tensor given to a launching call is checked here first; raw integer addresses
+# are the caller's responsibility.  The library's own checks (shapes, formats,
+# overlaps) still follow in C.
+
+def _check_tensor(t, name, dtype=None, min_bytes=None, tensors=None):
+    """Address of t after checking its dtype, contiguity and size (None and
+    int addresses pass through); t joins `tensors`, whose devices
+    _check_devices checks once every argument has passed these checks."""
+    import torch
+    if t is None or isinstance(t, int):
+        return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor or an integer address, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    nbytes = t.numel() * t.element_size()
+    if min_bytes is not None and min_bytes > 0 and nbytes < min_bytes:
+        raise ValueError(f"{name} holds {nbytes} bytes, the call reads {min_bytes}")
+    if tensors is not None:
+        tensors.append((name, t))
+    return t.data_ptr()
+
+
+def _check_view_tensor(v, name, tensors):
+    """An operand or dst given as a tensor joins the device check (its shape,
+    layout and overlap checks are the library's)."""
+    import torch
+    if isinstance(v, torch.Tensor):
+        if v.dtype != torch.float32:
+            raise TypeError(f"{name} must be torch.float32, got {v.dtype}")
+        tensors.append((name, v))
+
+
+def _check_devices(tensors):
+    """Every tensor on the GPU, all on the current device."""
+    import torch
+    devs = set()
+    for name, t in tensors:
+        if not t.is_cuda:
+            raise TypeError(f"{name}: tensor arguments of a launching call must be on the GPU")
+        devs.add(t.device.index)
+    if not devs:
+        return
+    if len(devs) > 1:
+        raise TypeError(f"tensor arguments are on different GPUs: {sorted(devs)}")
+    cur = torch.cuda.current_device()
+    if devs != {cur}:
+        raise TypeError(f"tensor arguments are on cuda:{devs.pop()}, the current device is cuda:{cur}")
+
+
+def _weight_bytes_or_none(wfmt, N, K):
+    try:
+        b = int(load().gemv_weight_bytes(_fmt(wfmt), N, K))
+    except (KeyError, TypeError, ctypes.ArgumentError):
+        return None
+    return b if b > 0 else None
+
+
+def _checked_product_args(W, wfmt, N, K, x, x_floats, views, W2=None):
+    """Checked addresses of W (and W2) and x for a product over x_floats
+    values of x; views are the operand / dst arguments."""
+    import torch
+    devices = []
+    wb = _weight_bytes_or_none(wfmt, N, K)
+    w = _check_tensor(W, "W", min_bytes=wb, tensors=devices)
+    w2 = _check_tensor(W2, "W_up", min_bytes=wb, tensors=devices)
+    xa = _check_tensor(x, "x", dtype=torch.float32,
+                       min_bytes=4 * x_floats if isinstance(x_floats, int) and x_floats > 0 else None,
+                       tensors=devices)
+    for name, v in views.items():
+        _check_view_tensor(v, name, devices)
+    _check_devices(devices)
+    return w, w2, xa
+
+
 def _fmt(wfmt):
     return FORMATS[wfmt] if isinstance(wfmt, str) else int(wfmt)
 
@@ -171,12 +252,50 @@ def _raise(status):
                     lib.gemv_last_hip_error() if status == STATUS_CODE["GEMV_E_HIP"] else 0)
 
 
+def _ncols_floats(ncols, K):
+    """x values a several-column call reads, or None where the library itself
+    rejects the column count (1..8) or K."""
+    if isinstance(ncols, int) and isinstance(K, int) and 1 <= ncols <= 8 and K > 0:
+        return ncols * K
+    return None
+
+
+def _int_or_none(v):
+    return v if isinstance(v, int) and v > 0 else None
+
+
+def _checked_fwht_args(x, signs, nrows, K, nsigns, dst):
+    import torch
+    devices = []
+    nx = nrows * K if _int_or_none(nrows) and _int_or_none(K) else None
+    xa = _check_tensor(x, "x", dtype=torch.float32, min_bytes=4 * nx if nx else None, tensors=devices)
+    sa = _check_tensor(signs, "signs", dtype=torch.float32,
+                       min_bytes=4 * nsigns if _int_or_none(nsigns) else None, tensors=devices)
+    da = _check_tensor(dst, "dst", dtype=torch.float32, min_bytes=4 * nx if nx else None, tensors=devices)
+    _check_devices(devices)
+    return xa, sa, da
+
+
+def _checked_fused_fwht_args(W, wfmt, N, K, x, signs, nsigns, mul_operand, add_operand, dst):
+    import torch
+    w, _, _ = _checked_product_args(W, wfmt, N, K, x, K, {"mul_operand": mul_operand, "add_operand": add_operand,
+                                                          "dst": dst})
+    devices = []
+    _check_view_tensor(x, "x", devices)
+    sa = _check_tensor(signs, "signs", dtype=torch.float32,
+                       min_bytes=4 * nsigns if _int_or_none(nsigns) else None, tensors=devices)
+    _check_devices(devices)
+    return w, sa
+
+
 # ------------------------------------------------------------------ API (C names)
 
 def gemv_fused(W, wfmt, N, K, x, act, mul_operand=None, add_operand=None, dst=None, stream=None):
     """dst = epilogue(W x) on the GPU (one launch, asynchronous on ``stream``;
     default: torch's current stream).  Raises GemvError on a rejected call."""
-    st = load().gemv_fused(_addr(W), _fmt(wfmt), N, K, _addr(x), _act(act), _as_view(mul_operand),
+    w, _, xa = _checked_product_args(W, wfmt, N, K, x, K, {"mul_operand": mul_operand, "add_operand": add_operand,
+                                                            "dst": dst})
+    st = load().gemv_fused(w, _fmt(wfmt), N, K, xa, _act(act), _as_view(mul_operand),
                            _as_view(add_operand), _as_view(dst), _stream(stream))
     if st != 0:
         _raise(st)
@@ -190,7 +309,14 @@ def gemv_validate(W, wfmt, N, K, x, act, mul_operand=None, add_operand=None, dst
 
 def gemv_epilogue(act, N, acc, mul_operand=None, add_operand=None, dst=None, stream=None):
     """dst = epilogue(acc) as a separate pass (the unfused path)."""
-    st = load().gemv_epilogue(_act(act), N, _addr(acc), _as_view(mul_operand), _as_view(add_operand),
+    import torch
+    devices = []
+    a = _check_tensor(acc, "acc", dtype=torch.float32,
+                      min_bytes=4 * N if isinstance(N, int) and N > 0 else None, tensors=devices)
+    for name, v in (("mul_operand", mul_operand), ("add_operand", add_operand), ("dst", dst)):
+        _check_view_tensor(v, name, devices)
+    _check_devices(devices)
+    st = load().gemv_epilogue(_act(act), N, a, _as_view(mul_operand), _as_view(add_operand),
                               _as_view(dst), _stream(stream))
     if st != 0:
         _raise(st)
@@ -203,8 +329,8 @@ def gemv_epilogue_validate(act, N, acc, mul_operand=None, add_operand=None, dst=
 
 def gemv_glu(W_gate, W_up, wfmt, N, K, x, act="silu", dst=None, stream=None):
     """dst = act(W_gate x) * (W_up x) in one launch (act: "silu" or "sigmoid")."""
-    st = load().gemv_glu(_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, _addr(x), _act(act), _as_view(dst),
-                         _stream(stream))
+    wg, wu, xa = _checked_product_args(W_gate, wfmt, N, K, x, K, {"dst": dst}, W2=W_up)
+    st = load().gemv_glu(wg, wu, _fmt(wfmt), N, K, xa, _act(act), _as_view(dst), _stream(stream))
     if st != 0:
         _raise(st)
 
@@ -217,8 +343,8 @@ def gemv_glu_validate(W_gate, W_up, wfmt, N, K, x, act="silu", dst=None) -> int:
 def gemv_glu_ncols(W_gate, W_up, wfmt, N, K, ncols, x, act="silu", dst=None, stream=None):
     """dst[b, i] = act((W_gate x_b)_i) * (W_up x_b)_i for ncols columns x_b =
     x[b] (x: [ncols, K] f32; dst: ncols * N f32 in [ncols][N] order), one launch."""
-    st = load().gemv_glu_ncols(_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, ncols, _addr(x), _act(act),
-                               _as_view(dst), _stream(stream))
+    wg, wu, xa = _checked_product_args(W_gate, wfmt, N, K, x, _ncols_floats(ncols, K), {"dst": dst}, W2=W_up)
+    st = load().gemv_glu_ncols(wg, wu, _fmt(wfmt), N, K, ncols, xa, _act(act), _as_view(dst), _stream(stream))
     if st != 0:
         _raise(st)
 
@@ -231,7 +357,9 @@ def gemv_glu_ncols_validate(W_gate, W_up, wfmt, N, K, ncols, x, act="silu", dst=
 def gemv_fused_ncols(W, wfmt, N, K, ncols, x, act, mul_operand=None, add_operand=None, dst=None, stream=None):
     """dst[b, i] = epilogue((W x_b)_i) for ncols columns x_b = x[b] (x: [ncols, K]
     f32; dst and operands: ncols * N f32 in [ncols][N] order), one launch."""
-    st = load().gemv_fused_ncols(_addr(W), _fmt(wfmt), N, K, ncols, _addr(x), _act(act), _as_view(mul_operand),
+    w, _, xa = _checked_product_args(W, wfmt, N, K, x, _ncols_floats(ncols, K), {"mul_operand": mul_operand,
+                                                            "add_operand": add_operand, "dst": dst})
+    st = load().gemv_fused_ncols(w, _fmt(wfmt), N, K, ncols, xa, _act(act), _as_view(mul_operand),
                                  _as_view(add_operand), _as_view(dst), _stream(stream))
     if st != 0:
         _raise(st)
@@ -257,7 +385,8 @@ def gemv_ncols_kernel(wfmt, N, K, ncols) -> str:
 
 def gemv_fwht_signed(x, signs, nrows, K, n, nsigns, dst, stream=None):
     """dst = n^-1/2 H_n (x * s) per block of n, for nrows rows of K f32 values."""
-    st = load().gemv_fwht_signed(_addr(x), _addr(signs), nrows, K, n, nsigns, _addr(dst), _stream(stream))
+    xa, sa, da = _checked_fwht_args(x, signs, nrows, K, nsigns, dst)
+    st = load().gemv_fwht_signed(xa, sa, nrows, K, n, nsigns, da, _stream(stream))
     if st != 0:
         _raise(st)
 
@@ -269,7 +398,8 @@ def gemv_fwht_signed_validate(x, signs, nrows, K, n, nsigns, dst) -> int:
 def gemv_fused_fwht(W, wfmt, N, K, x, signs, n, nsigns, act, mul_operand=None, add_operand=None, dst=None,
                     stream=None):
     """dst = epilogue(W . FWHT_n(x * s)) in one launch."""
-    st = load().gemv_fused_fwht(_addr(W), _fmt(wfmt), N, K, _addr(x), _addr(signs), n, nsigns, _act(act),
+    w, sa = _checked_fused_fwht_args(W, wfmt, N, K, x, signs, nsigns, mul_operand, add_operand, dst)
+    st = load().gemv_fused_fwht(w, _fmt(wfmt), N, K, _addr(x), sa, n, nsigns, _act(act),
                                 _as_view(mul_operand), _as_view(add_operand), _as_view(dst), _stream(stream))
     if st != 0:
         _raise(st)
@@ -298,9 +428,10 @@ class PreparedGlu:
 
     def __init__(self, W_gate, W_up, wfmt, N, K, x, act="silu", dst=None):
         self._lib = load()
+        wg, wu, xa = _checked_product_args(W_gate, wfmt, N, K, x, K, {"dst": dst}, W2=W_up)
         self._view = dst if isinstance(dst, GemvView) else make_view(dst)
         self._ptr = ctypes.pointer(self._view)
-        self._args = (_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, _addr(x), _act(act))
+        self._args = (wg, wu, _fmt(wfmt), N, K, xa, _act(act))
 
     def __call__(self, stream=None):
         st = self._lib.gemv_glu(*self._args, self._ptr, _stream(stream))
@@ -313,9 +444,10 @@ class PreparedGluNcols:
 
     def __init__(self, W_gate, W_up, wfmt, N, K, ncols, x, act="silu", dst=None):
         self._lib = load()
+        wg, wu, xa = _checked_product_args(W_gate, wfmt, N, K, x, _ncols_floats(ncols, K), {"dst": dst}, W2=W_up)
         self._view = make_view(dst)
         self._ptr = ctypes.pointer(self._view)
-        self._args = (_addr(W_gate), _addr(W_up), _fmt(wfmt), N, K, ncols, _addr(x), _act(act))
+        self._args = (wg, wu, _fmt(wfmt), N, K, ncols, xa, _act(act))
 
     def __call__(self, stream=None):
         st = self._lib.gemv_glu_ncols(*self._args, self._ptr, _stream(stream))
@@ -327,8 +459,10 @@ class PreparedCall:
     """A gemv_fused call with its views marshalled once, for tight loops and
     graph capture (the tensors must stay alive and in place)."""
 
-    def __init__(self, W, wfmt, N, K, x, act, mul_operand=None, add_operand=None, dst=None):
+    def __init__(self, W, wfmt, N, K, x, act, mul_operand=None, add_operand=None, dst=None, _x_floats=None):
         self._lib = load()
+        _checked_product_args(W, wfmt, N, K, x, K if _x_floats is None else (_x_floats or None),
+                              {"mul_operand": mul_operand, "add_operand": add_operand, "dst": dst})
         self._views = [None if v is None else (v if isinstance(v, GemvView) else make_view(v))
                        for v in (mul_operand, add_operand, dst)]
         self._ptrs = [None if v is None else ctypes.pointer(v) for v in self._views]
@@ -344,7 +478,7 @@ class PreparedNcols(PreparedCall):
     """A gemv_fused_ncols call with its views marshalled once."""
 
     def __init__(self, W, wfmt, N, K, ncols, x, act, mul_operand=None, add_operand=None, dst=None):
-        super().__init__(W, wfmt, N, K, x, act, mul_operand, add_operand, dst)
+        super().__init__(W, wfmt, N, K, x, act, mul_operand, add_operand, dst, _x_floats=_ncols_floats(ncols, K))
         self._args = (_addr(W), _fmt(wfmt), N, K, ncols, _addr(x), _act(act))
 
     def __call__(self, stream=None):
@@ -358,6 +492,7 @@ class PreparedFusedFwht(PreparedCall):
 
     def __init__(self, W, wfmt, N, K, x, signs, n, nsigns, act, mul_operand=None, add_operand=None, dst=None):
         super().__init__(W, wfmt, N, K, x, act, mul_operand, add_operand, dst)
+        _checked_fused_fwht_args(W, wfmt, N, K, x, signs, nsigns, mul_operand, add_operand, dst)
         self._args = (_addr(W), _fmt(wfmt), N, K, _addr(x), _addr(signs), n, nsigns, _act(act))
 
     def __call__(self, stream=None):
@@ -371,7 +506,8 @@ class PreparedFwht:
 
     def __init__(self, x, signs, nrows, K, n, nsigns, dst):
         self._lib = load()
-        self._args = (_addr(x), _addr(signs), nrows, K, n, nsigns, _addr(dst))
+        xa, sa, da = _checked_fwht_args(x, signs, nrows, K, nsigns, dst)
+        self._args = (xa, sa, nrows, K, n, nsigns, da)
 
     def __call__(self, stream=None):
         st = self._lib.gemv_fwht_signed(*self._args, _stream(stream))

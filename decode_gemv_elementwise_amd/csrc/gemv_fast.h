@@ -227,9 +227,13 @@ struct FwhtTile {
                 v[j] = k < K ? a : 0.0f;
             }
         }
-        const int s0 = min(k0, K - 1) % f.nsigns;
         if (f.nsigns % 16 == 0 && (reinterpret_cast<uintptr_t>(f.signs) & 15) == 0) {
-            // the lane's 16 signs are contiguous and 16-byte aligned
+            // The lane's 16 signs are contiguous and 16-byte aligned.  nsigns
+            // divides K here, so K is a multiple of 16 and so is every tile
+            // start k0: a lane inside the row starts at k0 <= K - 16, and a
+            // lane past the end (whose values are zero) is clamped to K - 16,
+            // so that s0 + 15 < nsigns for every lane.
+            const int s0 = min(k0, K - 16) % f.nsigns;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 sg = *reinterpret_cast<const f32x4 *>(f.signs + s0 + 4 * q);
@@ -239,7 +243,7 @@ struct FwhtTile {
                 v[4 * q + 3] *= sg.w;
             }
         } else {
-            int si = s0;
+            int si = min(k0, K - 1) % f.nsigns;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 v[j] *= f.signs[si];

@@ -13,7 +13,7 @@ through which rounding in the dot product reaches the output:
 with a = acc_i, A = sum_j |w_ij x_j| (the oracle's absacc), s = sigmoid(a):
 
     none      D = A
-    sigmoid   D = s (1 - s) A
+    sigmoid   D = s (1 - s) A                    (1 - s evaluated as sigmoid(-a))
     silu      D = |s (1 + a (1 - s))| A          (|silu'(a)| A)
     silu_mul  D = |m_i| |silu'(a)| A
     mul       D = |m_i| A
@@ -31,6 +31,24 @@ and 4-bit block formats, whose dequantised values are exact).
 import numpy as np
 
 FLT32_MIN_NORMAL = 2.0 ** -126
+
+# Health ratio: err / (depth u) with u = 2^-24 and depth the longest chain of
+# float32 roundings a correct implementation puts between the exact products
+# and an output (its per-lane sequential length plus log2 of the reduction
+# width).  The textbook bound for a recursive sum, |fl(sum) - sum| <=
+# gamma_n sum |terms| with gamma_n ~ n u, puts a correct kernel at a ratio of
+# O(1) on any data; a dropped or doubled weight, a wrong row or a layout slip
+# lands orders of magnitude above it.  HEALTH_C is the constant of that bound
+# the gate allows (the per-format tolerances stay the gate of record).
+HEALTH_C = 4.0
+UNIT_ROUNDOFF_F32 = 2.0 ** -24
+
+
+def health_bound(depth):
+    """Largest guarded error a correct float32 evaluation of depth chained
+    roundings may show: HEALTH_C * depth * 2^-24."""
+    return HEALTH_C * float(depth) * UNIT_ROUNDOFF_F32
+
 
 TOLERANCE = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "q8b32": 1e-4, "q4b32": 1e-4}
 
@@ -52,10 +70,12 @@ def error_scale(act, acc, absacc, m=None, r=None):
     A = np.asarray(absacc, dtype=np.float64).reshape(-1)
     if act == "none":
         return A.copy()
-    s = _sigmoid(a)
-    dsilu = np.abs(s * (1.0 + a * (1.0 - s)))
+    # 1 - sigmoid(a) taken as sigmoid(-a): the subtraction would cancel for
+    # large positive a (1 - s is then below the spacing of doubles near 1)
+    s, sm = _sigmoid(a), _sigmoid(-a)
+    dsilu = np.abs(s * (1.0 + a * sm))
     if act == "sigmoid":
-        return s * (1.0 - s) * A
+        return s * sm * A
     if act == "silu":
         return dsilu * A
     if act == "silu_mul":
@@ -99,11 +119,11 @@ def glu_error_scale(act, g, absg, u, absu):
     the two row sums' rounding), f = silu or sigmoid."""
     g = np.asarray(g, dtype=np.float64).reshape(-1)
     u = np.asarray(u, dtype=np.float64).reshape(-1)
-    s = _sigmoid(g)
+    s, sm = _sigmoid(g), _sigmoid(-g)
     if act == "silu":
-        f, df = g * s, s * (1.0 + g * (1.0 - s))
+        f, df = g * s, s * (1.0 + g * sm)
     elif act == "sigmoid":
-        f, df = s, s * (1.0 - s)
+        f, df = s, s * sm
     else:
         raise ValueError(act)
     return np.abs(df * u) * np.asarray(absg, dtype=np.float64).reshape(-1) + np.abs(f) * np.asarray(absu, dtype=np.float64).reshape(-1)

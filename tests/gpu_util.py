@@ -3,8 +3,27 @@ import numpy as np
 import torch
 
 import oracle
-from oracle.compare import TOLERANCE, compare
+from oracle.compare import TOLERANCE, compare, health_bound
 from decode_gemv_elementwise_amd import binding
+
+# Values per 16-byte chunk of W, per format.
+CHUNK_VALUES = {"f32": 4, "f16": 8, "bf16": 8, "q8b32": 16, "q4b32": 32}
+
+
+def lane_depth(fmt, K):
+    """Chained float32 roundings between the products and one output on the
+    vector-ALU kernels: a lane sums its ceil(K / (64 E)) chunks in order, each
+    chunk a chain of E products plus the fold and the scale (2 more), and the
+    64 lane sums meet in a 6-level tree."""
+    E = CHUNK_VALUES[fmt]
+    return -(-K // (64 * E)) * (E + 2) + 6
+
+
+def assert_healthy(res, fmt, K, tag):
+    """The health-ratio gate beside the per-format tolerance."""
+    bound = health_bound(lane_depth(fmt, K))
+    assert res["max_err"] <= bound, (f"{tag}: max_err {res['max_err']:.3e} above the health bound {bound:.3e} "
+                                     f"(ratio {res['max_err'] / (bound / 4.0):.1f}) at {res['argmax']}")
 
 
 def log(msg):
@@ -46,6 +65,7 @@ def check_parity(w, x, act, m=None, r=None, out_shape=None, inplace=False, tag="
     tol = TOLERANCE[w.fmt]
     assert np.all(np.isfinite(g)), f"{tag}: non-finite output"
     assert res["max_err"] <= tol, f"{tag}: max_err {res['max_err']:.3e} > {tol} at {res['argmax']} ({res})"
+    assert_healthy(res, w.fmt, w.K, tag)
     return g, y, res
 
 
@@ -72,4 +92,8 @@ def check_ncols(w, X, act, M=None, R=None, out_shape=None, inplace=False, tag=""
                   m=None if M is None else M.reshape(-1), r=None if R is None else R.reshape(-1))
     assert np.all(np.isfinite(g)), tag
     assert res["max_err"] <= TOLERANCE[w.fmt], f"{tag}: {res}"
+    # the matrix-core kernel carries x as two 16-bit pieces (2^-20 relative);
+    # the gate applies to the vector-ALU kernels, which keep x in float32
+    if binding.gemv_ncols_kernel(w.fmt, w.N, w.K, X.shape[0]) != "columns_matrix":
+        assert_healthy(res, w.fmt, w.K, tag)
     return g

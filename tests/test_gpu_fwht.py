@@ -189,3 +189,52 @@ def test_fused_fwht_rejects_generic_path_shapes():
     assert e.value.status == binding.STATUS_CODE["GEMV_E_DIM"]
     torch.cuda.synchronize()
     assert torch.all(dst == 7.0)
+
+
+def _signs_then_nan(s):
+    """The signs on the device followed by NaN: a read past the last sign
+    would turn a transformed value into NaN."""
+    buf = torch.full((s.size + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    buf[: s.size] = dev(s)
+    return buf
+
+
+@pytest.mark.parametrize("nrows,K,n", [(1, 256, 256), (2, 1536, 512), (1, 1040, 16), (3, 48, 16)])
+def test_fwht_sign_reads_stay_in_bounds(nrows, K, n):
+    """K not a multiple of the 1024-value tile, with nsigns = K or n (a
+    multiple of 16, the aligned 16-sign path): lanes past the end of the row
+    must not read past the sign vector."""
+    rng = np.random.default_rng(K + n)
+    for ns in sorted({K, n}):
+        x = rng.normal(size=(nrows, K)).astype(np.float32)
+        s = _signs(rng, ns)
+        log(f"fwht bounds rows={nrows} K={K} n={n} nsigns={ns}")
+        xd = dev(x.reshape(-1))
+        dst = torch.full((nrows * K,), float("nan"), dtype=torch.float32, device="cuda")
+        binding.gemv_fwht_signed(xd, _signs_then_nan(s), nrows, K, n, ns, dst)
+        torch.cuda.synchronize()
+        g = host(dst).reshape(nrows, K)
+        y, d = oracle.fwht_signed(x, s, n)
+        assert np.all(np.isfinite(g))
+        diff = np.abs(g.astype(np.float64) - y)
+        assert np.max(np.where(diff == 0, 0.0, diff / np.maximum(np.abs(y), d))) <= FWHT_TOLERANCE
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+@pytest.mark.parametrize("N,K,n", [(37, 1536, 512), (5, 256, 256)])
+def test_fused_fwht_sign_reads_stay_in_bounds(fmt, N, K, n):
+    rng = np.random.default_rng(N + K)
+    w = synth.random_weights(rng, fmt, N, K)
+    x = rng.normal(size=K).astype(np.float32)
+    r = rng.normal(size=N).astype(np.float32)
+    for ns in sorted({K, n}):
+        s = _signs(rng, ns)
+        log(f"fused fwht bounds fmt={fmt} N={N} K={K} n={n} nsigns={ns}")
+        dst = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        binding.gemv_fused_fwht(dev(w.data), fmt, N, K, dev(x), _signs_then_nan(s), n, ns, "add",
+                                add_operand=dev(r), dst=dst)
+        torch.cuda.synchronize()
+        g = host(dst)
+        y, acc, absacc = oracle.fwht_gemv_reference(fmt, N, K, w.data, x, s, n, "add", r=r)
+        assert np.all(np.isfinite(g))
+        assert compare(g, y, acc, absacc, "add", r=r)["max_err"] <= TOLERANCE[fmt]

@@ -10,7 +10,7 @@ torch = pytest.importorskip("torch")
 
 import oracle
 from decode_gemv_elementwise_amd import binding, synth
-from gpu_util import check_ncols, check_parity, dev, host, log, run_fused
+from gpu_util import assert_healthy, check_ncols, check_parity, dev, host, log, run_fused
 from oracle.compare import TOLERANCE, compare
 
 pytestmark = pytest.mark.gpu
@@ -146,6 +146,43 @@ def test_integer_exact_q4_and_f16():
     g, _ = run_fused(wf, x, "none")
     acc, _ = oracle.gemv("f16", N, K, wf.data, x)
     assert np.array_equal(g.astype(np.float64), acc)
+
+
+def _integer_weights(rng, fmt, N, K):
+    """Small integers, exact in every float format."""
+    W = rng.integers(-8, 9, size=(N, K))
+    if fmt == "f32":
+        data = W.astype(np.float32).view(np.uint8).reshape(-1)
+    elif fmt == "f16":
+        data = W.astype(np.float16).view(np.uint8).reshape(-1)
+    else:  # bf16: the upper half of the float32 pattern, exact for |w| <= 256
+        data = (W.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16).view(np.uint8).reshape(-1)
+    return synth.Weights(fmt, N, K, data)
+
+
+@pytest.mark.parametrize("fmt,N,K", [("bf16", 512, 4096), ("f32", 512, 4096), ("bf16", 64, 14336),
+                                     ("f16", 96, 4097), ("f32", 7, 40964), ("bf16", 33, 1000),
+                                     ("f32", 1000, 257)])
+def test_integer_exact_float_formats(fmt, N, K):
+    """Integer weights and x in {-3..3}: every partial sum, in any order, is
+    an integer below 2^24, so the float32 result equals the oracle's double
+    sum bit for bit -- on aligned rows (the chunked kernel) and on ragged K
+    (4097: f16 rows that are not whole 16-byte chunks; 40964: f32 x too long
+    to stage, both on the element-wise kernel), for every epilogue that keeps
+    integers (none, mul by an integer, add an integer)."""
+    log(f"integer exact {fmt} {N}x{K}")
+    rng = np.random.default_rng(N + K)
+    w = _integer_weights(rng, fmt, N, K)
+    x = rng.integers(-3, 4, size=K).astype(np.float32)
+    acc, _ = oracle.gemv(fmt, N, K, w.data, x)
+    assert np.all(np.abs(acc) < 2 ** 24)
+    g, _ = run_fused(w, x, "none")
+    assert np.array_equal(g.astype(np.float64), acc)
+    mi = rng.integers(-5, 6, size=N).astype(np.float32)
+    g, _ = run_fused(w, x, "mul", m=mi)
+    assert np.array_equal(g.astype(np.float64), acc * mi)
+    g, _ = run_fused(w, x, "add", r=mi)
+    assert np.array_equal(g.astype(np.float64), acc + mi)
 
 
 @pytest.mark.parametrize("fmt", synth.FORMATS)
@@ -470,6 +507,7 @@ def check_glu(wg, wu, x, act, tag):
     res = compare_glu(g, y, act, ga, gA, ua, uA)
     assert np.all(np.isfinite(g)), tag
     assert res["max_err"] <= TOLERANCE[wg.fmt], f"{tag}: {res}"
+    assert_healthy(res, wg.fmt, wg.K, tag)
     return g
 
 

@@ -14,7 +14,7 @@ import scipy.special
 import torch
 
 import oracle
-from oracle.compare import TOLERANCE, compare, error_scale, glu_error_scale
+from oracle.compare import TOLERANCE, compare, error_scale, glu_error_scale, health_bound
 from decode_gemv_elementwise_amd import synth
 
 U = 2.0 ** -53
@@ -300,19 +300,143 @@ def test_metric_zero_for_exact_and_scaled_for_perturbation():
     assert res["max_err"] == pytest.approx(3e-6) and res["max_plain_rel"] == np.inf
 
 
-def test_metric_error_scales():
-    a = np.array([0.0, 2.0, -3.0])
-    A = np.array([1.0, 2.0, 4.0])
-    m = np.array([2.0, -1.0, 0.5], dtype=np.float32)
-    r = np.array([-1.0, 0.0, 3.0], dtype=np.float32)
-    s = scipy.special.expit(a)
-    ds = s * (1 + a * (1 - s))
-    assert np.allclose(error_scale("sigmoid", a, A), s * (1 - s) * A)
-    assert np.allclose(error_scale("silu", a, A), np.abs(ds) * A)
-    assert np.allclose(error_scale("silu_mul", a, A, m=m), np.abs(m) * np.abs(ds) * A)
-    assert np.allclose(error_scale("mul", a, A, m=m), np.abs(m) * A)
-    assert np.allclose(error_scale("add", a, A, r=r), A + np.abs(r))
-    assert error_scale("silu", np.array([0.0]), np.array([1.0]))[0] == 0.5  # silu'(0) = 1/2
+def _fd(f, a, h):
+    """Richardson-extrapolated central difference of f at a (error O(h^4))."""
+    d1 = (f(a + h) - f(a - h)) / (2.0 * h)
+    d2 = (f(a + h / 2) - f(a - h / 2)) / h
+    return (4.0 * d2 - d1) / 3.0
+
+
+# silu'(a) = 0 where 1 + a + e^a = 0, i.e. a = -1 - W(1/e) (W: Lambert's function)
+SILU_STATIONARY = -1.2784645427610738
+FD_POINTS = np.concatenate([np.linspace(-30.0, 30.0, 121), [SILU_STATIONARY, 1e-3, -1e-3, 0.0]])
+
+
+def _d_sigmoid(a):
+    """Numerical derivative of the oracle's own sigmoid.  Right of 0 the
+    oracle's value is 1 - tiny and a difference there cancels, so the
+    derivative is taken at -a, where the values are small and carry full
+    precision (the logistic's derivative is even)."""
+    b = -abs(a)
+    return _fd(oracle.sigmoid, b, 1e-3 * max(1.0, abs(b)))
+
+
+def _d_silu(a):
+    return _fd(oracle.silu, a, 1e-3 * max(1.0, abs(a)))
+
+
+def test_metric_error_scales_match_finite_differences():
+    """D (oracle/compare.py, error_scale) is |dy/da| A, the first-order effect
+    of the dot product's rounding on the output: checked for every epilogue
+    against numerical derivatives of the oracle's own C sigmoid and silu (not
+    a restatement of the formulas), at a in [-30, 30], silu's stationary point
+    and around 0, to 1e-6 relative."""
+    A = 3.7
+    m, r = np.float32(-0.625), np.float32(1.5)
+    for a in FD_POINTS:
+        aa, AA = np.array([a]), np.array([A])
+        cases = {
+            "none": A * abs(_fd(lambda t: t, a, 1e-3)),
+            "sigmoid": A * abs(_d_sigmoid(a)),
+            "silu": A * abs(_d_silu(a)),
+            "silu_mul": A * abs(_fd(lambda t: oracle.silu(t) * float(m), a, 1e-3 * max(1.0, abs(a)))),
+            "mul": A * abs(_fd(lambda t: t * float(m), a, 1e-3)),
+        }
+        for act, want in cases.items():
+            got = error_scale(act, aa, AA, m=np.array([m]), r=None)[0]
+            if act in ("silu", "silu_mul") and abs(a - SILU_STATIONARY) < 1e-9:
+                # silu' = 0 there: both sides vanish (the difference quotient
+                # down to its own truncation error)
+                assert got < 1e-12 * A and want < 1e-12 * A, (act, a, got, want)
+                continue
+            assert got == pytest.approx(want, rel=1e-6, abs=1e-300), (act, a, got, want)
+        # add: the derivative part A plus |r|, the magnitude the final float32
+        # addition rounds against
+        got = error_scale("add", aa, AA, r=np.array([r]))[0]
+        assert got - abs(float(r)) == pytest.approx(A * abs(_fd(lambda t: t + float(r), a, 1e-3)), rel=1e-6)
+
+
+def test_metric_error_scale_catches_planted_derivative_slips():
+    """A sign slip in silu' (s (1 - a (1 - s))) or a sigmoid' written s (1 + s)
+    differs from the numerical derivatives by far more than the 1e-6 the pin
+    allows, away from a = 0 where they happen to agree."""
+    for a in (-4.0, -1.0, 2.5, 7.0):
+        s = 1.0 / (1.0 + np.exp(-a))
+        assert abs(abs(s * (1.0 - a * (1.0 - s))) - abs(_d_silu(a))) > 1e-3 * abs(_d_silu(a))
+        assert abs(s * (1.0 + s) - abs(_d_sigmoid(a))) > 1e-3 * abs(_d_sigmoid(a))
+
+
+def test_glu_metric_scale_matches_finite_differences():
+    """glu_error_scale is |dy/dg| A_g + |dy/du| A_u for y = f(g) u, checked
+    against numerical partial derivatives of the oracle's own silu and
+    sigmoid."""
+    Ag, Au = 2.25, 0.8
+    f = {"silu": oracle.silu, "sigmoid": oracle.sigmoid}
+    for act in ("silu", "sigmoid"):
+        for g in FD_POINTS:
+            for u in (-3.0, 0.5, 11.0):
+                if act == "sigmoid":
+                    dg = abs(_d_sigmoid(g) * u)
+                else:
+                    dg = abs(_fd(lambda t: f[act](t) * u, g, 1e-3 * max(1.0, abs(g))))
+                du = abs(_fd(lambda t: f[act](g) * t, u, 1e-3 * max(1.0, abs(u))))
+                want = dg * Ag + du * Au
+                got = glu_error_scale(act, np.array([g]), np.array([Ag]), np.array([u]), np.array([Au]))[0]
+                assert got == pytest.approx(want, rel=1e-6), (act, g, u, got, want)
+
+
+def _gpu_order_f32(w, x):
+    """float32 evaluation of W x in the vector-ALU kernels' documented order:
+    lane l sums its 16-byte chunks l, l + 64, ... (E values each) with one
+    rounding per product added, then the 64 lane sums meet pairwise in a
+    6-level tree.  A model of the order on the CPU, sharing nothing with the
+    kernels; numpy float64 products of float32 values are exact, each sum is
+    rounded to float32."""
+    N, K = w.shape
+    E = 8
+    nch = -(-K // E)
+    out = np.zeros(N, np.float32)
+    for i in range(N):
+        lanes = np.zeros(64, np.float32)
+        for c in range(nch):
+            l = c % 64
+            a = np.float32(lanes[l])
+            for e in range(c * E, min(K, c * E + E)):
+                a = np.float32(np.float64(a) + np.float64(w[i, e]) * np.float64(x[e]))
+            lanes[l] = a
+        v = lanes
+        while v.size > 1:
+            v = (v[: v.size // 2].astype(np.float64) + v[v.size // 2:].astype(np.float64)).astype(np.float32)
+        out[i] = v[0]
+    return out
+
+
+def test_health_gate_passes_a_correct_order_and_fails_a_dropped_weight():
+    """The health ratio (oracle/compare.py): a float32 evaluation in the
+    kernels' summation order sits inside HEALTH_C * depth * 2^-24, while a
+    result with a single weight dropped -- which the per-format f16 tolerance
+    of 2e-3 still accepts -- lands far outside it."""
+    rng = np.random.default_rng(51)
+    N, K = 24, 4096
+    wv = synth.random_weights(rng, "f16", N, K)
+    w16 = wv.data.view(np.float16).reshape(N, K).astype(np.float64)
+    x = synth.draw_vec(rng, K)
+    y, acc, absacc = oracle.reference("f16", N, K, wv.data, x, "none")
+    depth = -(-K // (64 * 8)) * (8 + 2) + 6
+    g = _gpu_order_f32(w16, x)
+    res = compare(g, y, acc, absacc, "none")
+    assert res["max_err"] <= health_bound(depth)
+    assert res["max_err"] / (depth * 2.0 ** -24) < 1.0  # the health ratio: O(1)
+    # drop a typical term of row 5 (its magnitude the row's median |w x|)
+    t = np.abs(w16[5] * x)
+    j = int(np.argsort(t)[K // 2])
+    w_drop = w16.copy()
+    w_drop[5, j] = 0.0
+    bad = (w_drop @ x.astype(np.float64)).astype(np.float32)
+    res_bad = compare(bad, y, acc, absacc, "none")
+    assert res_bad["max_err"] <= TOLERANCE["f16"]  # the north-star gate alone misses it
+    assert res_bad["max_err"] > 3 * health_bound(depth)
+    assert res_bad["argmax"] == 5
 
 
 def test_float32_rounding_of_oracle_passes_metric():
@@ -416,17 +540,6 @@ def test_glu_ncols_closed_forms_and_column_order():
     assert np.array_equal(Y1[0], y1)
     Ys, *_ = oracle.glu_ncols_reference("q4b32", N, K, wg.data, wu.data, X, "silu", rows=(7, 30))
     assert np.array_equal(Ys, Y[:, 7:30])
-
-
-def test_glu_metric_scale():
-    g = np.array([0.0, 1.5, -2.0])
-    u = np.array([2.0, -1.0, 0.5])
-    Ag = np.array([1.0, 2.0, 3.0])
-    Au = np.array([4.0, 5.0, 6.0])
-    s = scipy.special.expit(g)
-    d_silu = s * (1 + g * (1 - s))
-    assert np.allclose(glu_error_scale("silu", g, Ag, u, Au), np.abs(d_silu * u) * Ag + np.abs(g * s) * Au)
-    assert np.allclose(glu_error_scale("sigmoid", g, Ag, u, Au), np.abs(s * (1 - s) * u) * Ag + s * Au)
 
 
 # ----------------------------------------------------------------- several columns (ncols)
