@@ -1,25 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the fused-epilogue decode GEMV on one MI355X.
 
-A step is one pass of the whole path over one synthetic input: one
-gemv_fused call (validate + launch, x staged into LDS, W streamed from HBM,
-dequantised in registers, dot product, wave reduction, epilogue, store); for
-the 4-bit layer workload, the six calls of the layer.  Inputs are resident in
-HBM before timing starts.  W (and x, operands, dst) rotate over enough copies
-to exceed 512 MiB, so the 256 MB Infinity Cache cannot serve W from a
-previous step.  The timed steps are captured in one HIP graph and replayed
-between two HIP events recorded on the launch stream.
+A step is one pass of the whole path over one synthetic input: for the
+default workload (one 4-bit decode layer), the six gemv_fused calls of the
+layer, each staging x in LDS, streaming its W from HBM, dequantising in
+registers, reducing each row over its wave and applying its epilogue before
+the one store.  Inputs are resident in HBM before timing starts.  W (and x,
+the operands and dst) rotate over enough copies to exceed 512 MiB, so the
+256 MB Infinity Cache cannot serve W from a previous step.
+
+The timed steps are captured once into a HIP graph (the calls' host checks
+run at capture) and the graph is replayed between two HIP events recorded on
+the launch stream; the replay of exactly `steps` steps is timed `repeats`
+times and the line reports the median (and the minimum).  `--launch stream`
+launches every call from the host instead, host checks included.
 
 value = algorithmic bytes per step x steps / time, in GB/s, where algorithmic
 bytes = W in its storage format + 4K (x) + 4N per epilogue operand read + 4N
-(dst).  One JSON line on stdout.
+(dst).  One JSON line per workload on stdout.
 """
 import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -34,10 +41,10 @@ PEAK_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # dense f16 matrix-core peak (the matrix-core column kernel runs f16 MFMAs)
 PEAK_MFMA_F16_TFLOPS = 2500.0
 ROTATE_MIN_BYTES = 512 << 20
-DEFAULT_WORKLOAD = "f16_outproj_residual_4096"
-# the device code of the one-column kernel (the kernel the counter summaries
-# cover; entry points and host checks excluded): a summary stays valid while
-# these files are unchanged
+DEFAULT_WORKLOAD = "q4b32_decode_layer"
+# the device code of the one-column kernels (the kernels the counter and trace
+# summaries cover; entry points and host checks excluded): a summary stays
+# valid while these files are unchanged
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_gemv_elementwise_amd", "csrc", f)
                   for f in ("gemv_device.h", "gemv_fast.h")]
 PROFILES = os.path.join(ROOT, "profiles")
@@ -52,25 +59,38 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--repeats", type=int, default=7, help="timed replays of the `steps` steps (median reported)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD,
                    help="a workload name, or 'all' (one JSON line each)")
     p.add_argument("--launch", choices=["graph", "stream"], default="graph")
     p.add_argument("--unfused", action="store_true",
-                   help="time gemv_fused(none) + gemv_epilogue instead of the fused call")
+                   help="time gemv_fused(none) + gemv_epilogue as the primary figure instead of the fused call")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="CPU-oracle sample length (0 disables the cpu_baseline leg)")
-    p.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
+                   help="CPU-oracle sample length (0 disables the CPU legs)")
+    p.add_argument("--no-probe", action="store_true", help="skip the bandwidth probe and the floor measurements")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes, 5 times (calibrates the "
                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count), then exit")
     return p.parse_args()
 
 
-def copy_calibration(torch, nbytes):
+def probe_lib():
     import ctypes
     from decode_gemv_elementwise_amd import build as b
     lib = ctypes.CDLL(b.PROBE_LIB)
-    lib.hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.hbm_read_probe.argtypes = [vp, i64, vp, ctypes.c_int, vp]
+    lib.hbm_copy.argtypes = [vp, vp, i64, vp]
+    lib.hbm_read_floor.argtypes = [vp, i64, vp, ctypes.c_int, vp]
+    lib.hbm_read_floor_out_floats.argtypes = [i64, ctypes.c_int]
+    lib.hbm_read_floor_out_floats.restype = i64
+    lib.hbm_read_floor_shapes.restype = ctypes.c_int
+    lib.gemv_valu_floor.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
+    return lib
+
+
+def copy_calibration(torch, nbytes):
+    lib = probe_lib()
     nbytes = (nbytes + 15) // 16 * 16
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.zeros_like(src)
@@ -95,6 +115,14 @@ def kernel_sha():
 
 def align(v, a=256):
     return (v + a - 1) // a * a
+
+
+def call_bytes(wl, c):
+    w = wl.weights[c.w]
+    ops = (1 if c.m else 0) + (1 if c.r else 0)
+    w2 = wl.weights[c.w2].data.size if c.w2 else 0
+    signs = 4 * wl.vectors[c.fwht[0]].size if c.fwht else 0
+    return w.data.size + w2 + signs + c.ncols * (4 * w.K + 4 * w.N * ops + 4 * w.N)
 
 
 class Step:
@@ -132,7 +160,7 @@ class Step:
         self.prepared = []
         for i in range(R):
             self.prepared.append(self._prepare_set(binding, i, unfused))
-        self.bytes_per_step = sum(self.call_bytes(c) for c in self.calls)
+        self.bytes_per_step = sum(call_bytes(wl, c) for c in self.calls)
 
     def _vec(self, name, i, shape=None):
         if name is None:
@@ -202,13 +230,6 @@ class Step:
                                                 dst=dst))
         return fns
 
-    def call_bytes(self, c):
-        w = self.wl.weights[c.w]
-        ops = (1 if c.m else 0) + (1 if c.r else 0)
-        w2 = self.wl.weights[c.w2].data.size if c.w2 else 0
-        signs = 4 * self.wl.vectors[c.fwht[0]].size if c.fwht else 0
-        return w.data.size + w2 + signs + c.ncols * (4 * w.K + 4 * w.N * ops + 4 * w.N)
-
     def launches_per_step(self):
         return len(self.prepared[0])
 
@@ -230,10 +251,12 @@ def run_steps(step, n, offset=0):
             fn()
 
 
-def time_steps(torch, step, steps, warmup, launch):
-    """Returns elapsed seconds for `steps` steps after `warmup` untimed ones,
-    measured with HIP events on the stream the kernels are launched on."""
+def time_steps(torch, step, steps, warmup, launch, repeats):
+    """Seconds for exactly `steps` steps, once per repeat, after `warmup`
+    untimed ones; each timed region is bracketed by device synchronisations
+    and measured with HIP events on the stream the kernels are launched on."""
     stream = torch.cuda.Stream()
+    out = []
     with torch.cuda.stream(stream):
         run_steps(step, 1)  # first launch outside any capture
         torch.cuda.synchronize()
@@ -248,29 +271,32 @@ def time_steps(torch, step, steps, warmup, launch):
             torch.cuda.synchronize()
             if gw is not None:
                 gw.replay()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            gt.replay()
-            e1.record(stream)
+            for _ in range(repeats):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                gt.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                out.append(e0.elapsed_time(e1) / 1e3)
+            del gt, gw
         else:
             run_steps(step, warmup)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            run_steps(step, steps, offset=warmup)
-            e1.record(stream)
-        torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1e3
+            for _ in range(repeats):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                run_steps(step, steps, offset=warmup)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                out.append(e0.elapsed_time(e1) / 1e3)
+    return out
 
 
 def probe_bandwidth(torch, nbytes=2 << 30):
-    import ctypes
-    from decode_gemv_elementwise_amd import build as b
-    lib = ctypes.CDLL(b.PROBE_LIB)
-    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib = probe_lib()
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     blocks = 2048
     out = torch.zeros(blocks, dtype=torch.float32, device="cuda")
@@ -292,87 +318,184 @@ def probe_bandwidth(torch, nbytes=2 << 30):
     return nbytes / sec / 1e9, ok
 
 
-def read_once_us(torch, nbytes, steps, warmup, store=False):
-    """Per-launch time of a kernel that only reads nbytes (one pass, every
-    load issued at once), over rotating buffers totalling more than 512 MiB
-    and replayed as a graph on its own stream, like the GEMV timing: the
-    shortest launch any kernel reading that many bytes can have here.  With
-    store, every wave also writes one result at the end, as a GEMV must."""
-    import ctypes
-    from decode_gemv_elementwise_amd import build as b
-    lib = ctypes.CDLL(b.PROBE_LIB)
-    fn = lib.hbm_read_once_store if store else lib.hbm_read_once
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
-    lib.hbm_read_once_blocks.argtypes = [ctypes.c_int64]
+def replay_us(torch, launch_one, n, repeats=3):
+    """Median per-launch microseconds of n launches captured in one graph on a
+    stream of its own, replayed `repeats` times; launch_one(i, stream) issues
+    launch i."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        launch_one(0, stream.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                launch_one(i, stream.cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e3 / n)
+    del g
+    return float(np.median(t))
+
+
+def read_floor_us(torch, nbytes, n):
+    """Per-launch time of reading nbytes and storing one result per wave, in
+    each of the probe library's launch shapes, over rotating buffers totalling
+    more than 512 MiB, replayed as a graph like the GEMV: {shape: us}."""
+    lib = probe_lib()
     nbytes = (nbytes + 15) // 16 * 16
     slot = (nbytes + 4095) // 4096 * 4096
     copies = max(2, -(-(512 << 20) // slot))
     buf = torch.ones(copies * slot // 4, dtype=torch.float32, device="cuda")
-    out = torch.zeros(4 * lib.hbm_read_once_blocks(nbytes), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        s = stream.cuda_stream
-        assert fn(buf.data_ptr(), nbytes, out.data_ptr(), s) == 0
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(warmup + steps):
-                fn(buf.data_ptr() + (i % copies) * slot, nbytes, out.data_ptr(), s)
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (warmup + steps)
-    del g, buf, out
+    res = {}
+    names = {0: "one pass, 4-wave workgroups, 8 loads per lane",
+             1: "one pass, 16-wave workgroups, 4 loads per lane",
+             2: "resident grid, 16-wave workgroups, 4 loads per lane per step"}
+    for shape in range(lib.hbm_read_floor_shapes()):
+        out = torch.zeros(int(lib.hbm_read_floor_out_floats(nbytes, shape)), dtype=torch.float32, device="cuda")
+
+        def one(i, s, shape=shape, out=out):
+            rc = lib.hbm_read_floor(buf.data_ptr() + (i % copies) * slot, nbytes, out.data_ptr(), shape, s)
+            assert rc == 0, rc
+        res[names.get(shape, str(shape))] = round(replay_us(torch, one, n), 3)
+        del out
+    del buf
     torch.cuda.empty_cache()
-    return us
+    return res
+
+
+def valu_floor_us(torch, fmt, N, K, n):
+    """Per-launch time of the one-column kernel's arithmetic alone for an
+    N x K call (the probe library's gemv_valu_floor): no weight byte read."""
+    from decode_gemv_elementwise_amd import binding
+    lib = probe_lib()
+    x = torch.ones(64, dtype=torch.float32, device="cuda")
+    out = torch.zeros(N, dtype=torch.float32, device="cuda")
+
+    def one(i, s):
+        assert lib.gemv_valu_floor(binding.FORMATS[fmt], N, K, x.data_ptr(), out.data_ptr(), s) == 0
+    return round(replay_us(torch, one, n), 3)
+
+
+def stream_us_per_call(torch, fns, n=400):
+    """Host-inclusive microseconds per call: prepared calls (one per rotating
+    set, taken in turn) launched n times back to back from Python on one
+    stream, timed on the host: the library's argument checks, the launch, the
+    Python/ctypes marshalling and the kernel itself."""
+    for i in range(20):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / n * 1e6
+
+
+# ------------------------------------------------------------------ CPU legs
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_threads():
+    """The threads this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS where that is set (the GPU machine's share of the host)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def _oracle_call(oracle, wl, c, outputs, rows=None):
+    w = wl.weights[c.w]
+    x = outputs[c.x[1:]] if c.x.startswith("@") else wl.vectors[c.x]
+    m = (outputs[c.m[1:]] if c.m.startswith("@") else wl.vectors[c.m]) if c.m else None
+    r = wl.vectors[c.r] if c.r else None
+    if c.w2 and c.ncols > 1:
+        return oracle.glu_ncols_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data,
+                                          np.reshape(x, (c.ncols, w.K)), c.act, rows=rows)[0]
+    if c.w2:
+        return oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act, rows=rows)[0]
+    if c.fwht:
+        return oracle.fwht_gemv_reference(w.fmt, w.N, w.K, w.data, x, wl.vectors[c.fwht[0]], c.fwht[1], c.act,
+                                          m=m, r=r, rows=rows)[0]
+    if c.ncols > 1:
+        M = None if m is None else np.reshape(m, (c.ncols, w.N))
+        R = None if r is None else np.reshape(r, (c.ncols, w.N))
+        return oracle.ncols_reference(w.fmt, w.N, w.K, w.data, np.reshape(x, (c.ncols, w.K)), c.act,
+                                      M=M, R=R, rows=rows)[0]
+    return oracle.reference(w.fmt, w.N, w.K, w.data, x, c.act, m=m, r=r, rows=rows)[0]
+
+
+def _oracle_step(oracle, wl, threads, pool):
+    """One pass of the workload through the oracle; with threads > 1 each call's
+    rows are split into contiguous ranges run concurrently (the C oracle runs
+    without the interpreter lock), so every row is computed by the same code
+    in the same order as with one thread."""
+    outputs = {}
+    for c in wl.calls:
+        N = wl.weights[c.w].N
+        if threads == 1:
+            y = _oracle_call(oracle, wl, c, outputs)
+        else:
+            bounds = [(N * k // threads, N * (k + 1) // threads) for k in range(threads)]
+            parts = list(pool.map(lambda b: _oracle_call(oracle, wl, c, outputs, rows=b),
+                                  [b for b in bounds if b[1] > b[0]]))
+            y = np.concatenate(parts, axis=-1)
+        outputs[c.name] = np.asarray(y).astype(np.float32).reshape(-1)
+    return outputs
 
 
 def cpu_baseline(wl, seconds):
-    """The oracle as written (single thread, double precision), on full calls of
-    the same workload, for about `seconds` of CPU time."""
+    """The oracle as written (double precision, every row, each epilogue as its
+    own pass) on the GPU machine's host over full steps of the same workload: on
+    one thread for about `seconds`, then row-partitioned over every host
+    thread for about half that; both runs give bit-identical outputs."""
     import oracle
-    calls = wl.calls
-    outputs = {}
-    t0 = time.perf_counter()
-    nbytes = 0
-    ncalls = 0
-    while True:
-        for c in calls:
-            w = wl.weights[c.w]
-            x = outputs[c.x[1:]] if c.x.startswith("@") else wl.vectors[c.x]
-            m = (outputs[c.m[1:]] if c.m.startswith("@") else wl.vectors[c.m]) if c.m else None
-            r = wl.vectors[c.r] if c.r else None
-            if c.w2 and c.ncols > 1:
-                y = oracle.glu_ncols_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data,
-                                               np.reshape(x, (c.ncols, w.K)), c.act)[0].reshape(-1)
-            elif c.w2:
-                y = oracle.glu_reference(w.fmt, w.N, w.K, w.data, wl.weights[c.w2].data, x, c.act)[0]
-            elif c.fwht:
-                y = oracle.fwht_gemv_reference(w.fmt, w.N, w.K, w.data, x, wl.vectors[c.fwht[0]], c.fwht[1], c.act,
-                                               m=m, r=r)[0]
-            elif c.ncols > 1:
-                y = oracle.ncols_reference(w.fmt, w.N, w.K, w.data, np.reshape(x, (c.ncols, w.K)), c.act,
-                                           M=m, R=r)[0].reshape(-1)
-            else:
-                y, _, _ = oracle.reference(w.fmt, w.N, w.K, w.data, x, c.act, m=m, r=r)
-            outputs[c.name] = y.astype(np.float32)
-            ops = (1 if c.m else 0) + (1 if c.r else 0)
-            w2 = wl.weights[c.w2].data.size if c.w2 else 0
-            signs = 4 * wl.vectors[c.fwht[0]].size if c.fwht else 0
-            nbytes += w.data.size + w2 + signs + c.ncols * (4 * w.K + 4 * w.N * ops + 4 * w.N)
-            ncalls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{ncalls} full calls of {wl.name} (every row, double accumulation, "
-                      f"separate epilogue pass) in {el:.1f} s on one host thread",
-            "us_per_call": round(el / ncalls * 1e6, 1)}
+    step_bytes = sum(call_bytes(wl, c) for c in wl.calls)
+    res = {}
+    ref = None
+    threads_all = host_threads()
+    for threads, budget in ((1, seconds), (threads_all, seconds / 2)):
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            t0 = time.perf_counter()
+            steps = 0
+            while True:
+                out = _oracle_step(oracle, wl, threads, pool)
+                steps += 1
+                el = time.perf_counter() - t0
+                if el >= budget:
+                    break
+        if ref is None:
+            ref = out
+        same = all(np.array_equal(ref[k].view(np.uint32), out[k].view(np.uint32)) for k in ref)
+        res[threads] = (steps, el, same)
+    steps1, el1, _ = res[1]
+    stepsn, eln, same = res[threads_all]
+    return {"value": round(step_bytes * steps1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps1} full steps of {wl.name} ({len(wl.calls)} calls each: every row, double "
+                      f"accumulation, separate epilogue pass) in {el1:.1f} s on one host thread",
+            "us_per_step": round(el1 / steps1 * 1e6, 1),
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "all_cores": {"value": round(step_bytes * stepsn / eln / 1e9, 4), "unit": "GB/s",
+                          "threads": threads_all, "us_per_step": round(eln / stepsn * 1e6, 1),
+                          "sample": f"{stepsn} full steps in {eln:.1f} s, each call's rows split over "
+                                    f"{threads_all} threads", "bitwise_equal_to_one_thread": bool(same)}}
 
 
 def cpu_fused_baseline(wl, seconds):
@@ -384,7 +507,7 @@ def cpu_fused_baseline(wl, seconds):
         return None
     if any(c.w2 or c.ncols > 1 or c.fwht for c in wl.calls):
         return None
-    threads = len(os.sched_getaffinity(0))
+    threads = host_threads()
     out = {}
     for fused in (True, False):
         outputs = {}
@@ -412,11 +535,9 @@ def cpu_fused_baseline(wl, seconds):
                       f"{threads} host threads"}
 
 
-def read_counters(workload):
-    """Per-launch HBM traffic (bytes) from the committed rocprofv3 counter
-    summary of this workload's dominant kernel, if it was taken on the current
-    kernel source; else None."""
-    path = os.path.join(PROFILES, f"counters_{workload}.txt")
+# ------------------------------------------------------------------ committed profiles
+
+def _read_summary(path):
     if not os.path.exists(path):
         return None
     kv = {}
@@ -426,10 +547,65 @@ def read_counters(workload):
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256") != kernel_sha():
         return None
+    return kv
+
+
+def read_counters(workload):
+    """Per-launch HBM traffic (bytes) of this workload's dominant kernel from
+    the committed rocprofv3 counter summary, if it was taken on the current
+    kernel source; else None."""
+    kv = _read_summary(os.path.join(PROFILES, f"counters_{workload}.txt"))
     try:
-        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+        return None if kv is None else float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_trace(workload):
+    """Average device duration (us) of this workload's dominant kernel from the
+    committed rocprofv3 kernel-trace summary, if it was taken on the current
+    kernel source; else None."""
+    kv = _read_summary(os.path.join(PROFILES, f"trace_{workload}.txt"))
+    try:
+        return None if kv is None else float(kv["dominant_kernel_avg_ns"]) / 1e3
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ one workload
+
+def _alone(synth, wl, dom):
+    """The dominant call as a workload of its own; inputs that earlier calls
+    of the step produce become fresh vectors of the same length (timing only)."""
+    vecs = dict(wl.vectors)
+    w = wl.weights[dom.w]
+    x, m = dom.x, dom.m
+    if x.startswith("@"):
+        x = "_x_alone"
+        vecs[x] = synth.draw_vec(np.random.default_rng(1), dom.ncols * w.K)
+    if m and m.startswith("@"):
+        m = "_m_alone"
+        vecs[m] = synth.draw_vec(np.random.default_rng(2), dom.ncols * w.N)
+    alone = synth.Call(dom.name, dom.w, x, dom.act, m=m, r=dom.r, out_shape=dom.out_shape,
+                       inplace=dom.inplace, w2=dom.w2, ncols=dom.ncols, fwht=dom.fwht)
+    ws = {dom.w: w}
+    if dom.w2:
+        ws[dom.w2] = wl.weights[dom.w2]
+    return synth.Workload(wl.name, ws, vecs, [alone])
+
+
+def _kernel_name(binding, dom, w, cols_kernel):
+    if dom.w2 and dom.ncols > 1:
+        return (f"gemv_cols_mfma_kernel<{w.fmt}, ncols={dom.ncols}> x2, gated pair as up then gate ({dom.name})"
+                if cols_kernel == "columns_matrix" and dom.act == "silu" else
+                f"gemv_cols(_tiles)_kernel<{w.fmt}, ncols={dom.ncols}, gated pair> ({dom.name})")
+    if cols_kernel == "columns_matrix":
+        return f"gemv_cols_mfma_kernel<{w.fmt}, ncols={dom.ncols}> ({dom.name})"
+    if dom.ncols > 1:
+        return f"gemv_cols_kernel<{w.fmt}, ncols={dom.ncols}> ({dom.name})"
+    if dom.fwht:
+        return f"gemv_fast_kernel<{w.fmt}, signed Hadamard prologue> ({dom.name})"
+    return f"gemv_fast_kernel<{w.fmt}{', gated pair' if dom.w2 else ''}> ({dom.name})"
 
 
 def bench_workload(torch, binding, synth, name, args, probe):
@@ -438,53 +614,41 @@ def bench_workload(torch, binding, synth, name, args, probe):
     step = Step(torch, binding, wl, args.unfused)
     log(f"  {step.copies} copies, {step.launches_per_step()} launches/step, "
         f"{step.bytes_per_step} algorithmic bytes/step")
-    sec = time_steps(torch, step, args.steps, args.warmup, args.launch)
+    secs = time_steps(torch, step, args.steps, args.warmup, args.launch, args.repeats)
+    sec = float(np.median(secs))
     ms_per_step = sec / args.steps * 1e3
     value = step.bytes_per_step * args.steps / sec / 1e9
+    log(f"  {ms_per_step * 1e3:.3f} us/step (median of {len(secs)}), min {min(secs) / args.steps * 1e6:.3f}")
 
-    # dominant kernel: the call with the most bytes; timed alone the same way
-    dom = max(wl.calls, key=step.call_bytes)
+    # the same step with every epilogue as a separate pass (the fusion effect)
+    other = None
+    if any(c.act != "none" or c.w2 or c.fwht for c in wl.calls):
+        ostep = Step(torch, binding, wl, not args.unfused)
+        osecs = time_steps(torch, ostep, args.steps, args.warmup, args.launch, args.repeats)
+        other = {"us_per_step": round(float(np.median(osecs)) / args.steps * 1e6, 3),
+                 "launches_per_step": ostep.launches_per_step()}
+        del ostep
+
+    # dominant kernel: the call with the most bytes, timed alone the same way
+    dom = max(wl.calls, key=lambda c: call_bytes(wl, c))
     if len(wl.calls) == 1 and step.launches_per_step() == 1:
-        dom_sec = sec / args.steps
+        dom_secs = [s / args.steps for s in secs]
+        dstep = step
     else:
-        # inputs produced by earlier calls of the step become fresh vectors of
-        # the same length (timing only)
-        vecs = dict(wl.vectors)
-        w = wl.weights[dom.w]
-        x, m = dom.x, dom.m
-        if x.startswith("@"):
-            x = "_x_alone"
-            vecs[x] = synth.draw_vec(np.random.default_rng(1), dom.ncols * w.K)
-        if m and m.startswith("@"):
-            m = "_m_alone"
-            vecs[m] = synth.draw_vec(np.random.default_rng(2), dom.ncols * w.N)
-        alone = synth.Call(dom.name, dom.w, x, dom.act, m=m, r=dom.r, out_shape=dom.out_shape,
-                           inplace=dom.inplace, w2=dom.w2, ncols=dom.ncols, fwht=dom.fwht)
-        ws = {dom.w: w}
-        if dom.w2:
-            ws[dom.w2] = wl.weights[dom.w2]
-        sub = synth.Workload(wl.name, ws, vecs, [alone])
-        dstep = Step(torch, binding, sub, False)
-        dom_sec = time_steps(torch, dstep, args.steps, args.warmup, args.launch) / args.steps
-        del dstep
-    dom_bytes = step.call_bytes(dom)
+        dstep = Step(torch, binding, _alone(synth, wl, dom), False)
+        dom_secs = [s / args.steps for s in time_steps(torch, dstep, args.steps, args.warmup, args.launch,
+                                                       args.repeats)]
+    dom_sec = float(np.median(dom_secs))
+    stream_us = (stream_us_per_call(torch, [p[0] for p in dstep.prepared]) if dstep.launches_per_step() == 1
+                 else None)
+    del dstep
+    dom_bytes = call_bytes(wl, dom)
     dom_w = wl.weights[dom.w]
     dom_flops = 2 * dom_w.N * dom_w.K * dom.ncols * (2 if dom.w2 else 1)
     achieved = dom_bytes / dom_sec / 1e9
     cols_kernel = binding.gemv_ncols_kernel(dom_w.fmt, dom_w.N, dom_w.K, dom.ncols) if dom.ncols > 1 else None
-    if dom.w2 and dom.ncols > 1:
-        kernel_name = (f"gemv_cols_mfma_kernel<{dom_w.fmt}, ncols={dom.ncols}> x2, gated pair as up then gate ({dom.name})"
-                       if cols_kernel == "columns_matrix" and dom.act == "silu" else
-                       f"gemv_cols(_tiles)_kernel<{dom_w.fmt}, ncols={dom.ncols}, gated pair> ({dom.name})")
-    elif cols_kernel == "columns_matrix":
-        kernel_name = f"gemv_cols_mfma_kernel<{dom_w.fmt}, ncols={dom.ncols}> ({dom.name})"
-    elif dom.ncols > 1:
-        kernel_name = f"gemv_cols_kernel<{dom_w.fmt}, ncols={dom.ncols}> ({dom.name})"
-    elif dom.fwht:
-        kernel_name = f"gemv_fast_kernel<{dom_w.fmt}, signed Hadamard prologue> ({dom.name})"
-    else:
-        kernel_name = f"gemv_fast_kernel<{dom_w.fmt}{', gated pair' if dom.w2 else ''}> ({dom.name})"
     traffic = read_counters(name)
+    trace_us = read_trace(name)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -505,17 +669,23 @@ def bench_workload(torch, binding, synth, name, args, probe):
              **({"prologue": f"signed FWHT n={c.fwht[1]}"} if c.fwht else {})}
             for c in wl.calls],
             "fused": not args.unfused, "launches_per_step": step.launches_per_step(),
-            "launch": args.launch, "rotating_copies": step.copies,
+            "launch": args.launch, "rotating_copies": step.copies, "repeats": args.repeats,
             "algorithmic_bytes_per_step": step.bytes_per_step},
         "us_per_step": round(ms_per_step * 1e3, 3),
+        "us_per_step_min": round(min(secs) / args.steps * 1e6, 3),
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": kernel_name,
+                     "kernel": _kernel_name(binding, dom, dom_w, cols_kernel),
                      "algorithmic_bytes_per_launch": dom_bytes,
-                     "us_per_launch": round(dom_sec * 1e6, 3)},
+                     "us_per_launch": round(dom_sec * 1e6, 3),
+                     "us_per_launch_min": round(min(dom_secs) * 1e6, 3),
+                     "trace_us_per_launch": None if trace_us is None else round(trace_us, 3),
+                     "stream_us_per_call": None if stream_us is None else round(stream_us, 3)},
     }
+    if other is not None:
+        res["unfused" if not args.unfused else "fused_step"] = other
     # one FMA per weight and destination column: where that work at the peak
     # of the units that run it (the matrix cores for the matrix-core column
     # kernel, else the vector ALUs) takes longer than the bytes at the HBM
@@ -530,15 +700,19 @@ def bench_workload(torch, binding, synth, name, args, probe):
     if probe is not None:
         res["probe_read_gbps"] = round(probe, 1)
         res["roofline"]["frac_of_probe"] = round(achieved / probe, 4)
-        # the same bytes read by a kernel that does nothing else: what the
-        # launch and the stream alone cost at this size
-        floor_us = read_once_us(torch, dom_bytes, args.steps, args.warmup)
-        res["roofline"]["same_size_read_us"] = round(floor_us, 3)
-        res["roofline"]["frac_of_same_size_read"] = round(floor_us / (dom_sec * 1e6), 4)
-        # ... and then one store per wave, which every GEMV launch also waits for
-        floor_st_us = read_once_us(torch, dom_bytes, args.steps, args.warmup, store=True)
-        res["roofline"]["same_size_read_store_us"] = round(floor_st_us, 3)
-        res["roofline"]["frac_of_same_size_read_store"] = round(floor_st_us / (dom_sec * 1e6), 4)
+        # the same bytes read by kernels that do nothing else, each wave then
+        # storing one result as a GEMV launch must: the best of three launch
+        # shapes is what the launch and the stream alone cost at this size
+        floors = read_floor_us(torch, dom_bytes, max(50, min(args.steps, 400)))
+        floor_us = min(floors.values())
+        res["roofline"]["same_size_read_store_us"] = floor_us
+        res["roofline"]["same_size_read_store_by_shape_us"] = floors
+        res["roofline"]["frac_of_same_size_read_store"] = round(floor_us / (dom_sec * 1e6), 4)
+        res["roofline"]["frac_of_peak_at_floor"] = round(dom_bytes / (floor_us * 1e3) / PEAK_HBM_GBPS, 4)
+        if dom.ncols == 1 and not dom.w2 and not dom.fwht:
+            # the kernel's arithmetic alone, no weight byte read
+            res["roofline"]["valu_floor_us"] = valu_floor_us(torch, dom_w.fmt, dom_w.N, dom_w.K,
+                                                             max(50, min(args.steps, 400)))
     del step
     torch.cuda.empty_cache()
     return res, wl
@@ -552,8 +726,8 @@ def main():
               "library (row or K sharding is described in the design notes); use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
-    if args.steps < 1 or args.warmup < 0:
-        sys.exit("steps must be >= 1 and warmup >= 0")
+    if args.steps < 1 or args.warmup < 0 or args.repeats < 1:
+        sys.exit("steps and repeats must be >= 1 and warmup >= 0")
     import torch
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
@@ -571,9 +745,9 @@ def main():
     for i, name in enumerate(names):
         res, wl = bench_workload(torch, binding, synth, name, args, probe)
         if i == 0 and args.cpu_seconds > 0:
-            log("cpu baseline (oracle)")
+            log("cpu baseline (oracle, one thread, then every host thread)")
             res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-            log("cpu comparison (tile-fused GEMV, all host cores)")
+            log("cpu comparison (tile-fused GEMV, every host thread)")
             res["cpu_fused"] = cpu_fused_baseline(wl, args.cpu_seconds / 2)
         print(json.dumps(res), flush=True)
 

@@ -42,11 +42,11 @@ def _run(cmd, verbose):
         raise RuntimeError(f"build step failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
 
 
-def _compile(sources, out, verbose, extra_flags=()):
+def _compile(sources, out, verbose):
     """Compiles each source to an object (in parallel), then links them."""
     with tempfile.TemporaryDirectory(prefix="gemv_build_") as tmpdir:
         objs = [os.path.join(tmpdir, f"{i}_{os.path.basename(src)}.o") for i, src in enumerate(sources)]
-        cmds = [[HIPCC, *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c", "-o", o, src]
+        cmds = [[HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", "-o", o, src]
                 for src, o in zip(sources, objs)]
         with ThreadPoolExecutor(max(1, min(len(cmds), 4))) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
@@ -63,12 +63,12 @@ def build_cpu(verbose: bool = False) -> str:
     return CPU_LIB
 
 
-def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
+def build(verbose: bool = False) -> str:
     """Builds the GEMV library, the benchmark's measurement library and the
     CPU comparison GEMV."""
     _compile(PROBE_SOURCES, PROBE_LIB, verbose)
     build_cpu(verbose)
-    return _compile(SOURCES, out, verbose, extra_flags)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

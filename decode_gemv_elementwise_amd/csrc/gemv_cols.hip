@@ -41,72 +41,36 @@
 namespace gemv {
 namespace {
 
-// Tuning: waves per workgroup, the x-staging budget that sets the segment
-// length, and the chunk loads per lane a batch aims for.
-#ifndef GEMV_COLS_WAVES
-#define GEMV_COLS_WAVES 4
-#endif
-#ifndef GEMV_COLS_X_BUDGET
-#define GEMV_COLS_X_BUDGET 64
-#endif
-#ifndef GEMV_COLS_LOADS
-#define GEMV_COLS_LOADS 8
-#endif
-#ifndef GEMV_COLS_SERIAL
-#define GEMV_COLS_SERIAL 1
-#endif
-#ifndef GEMV_COLS_ONESHOT
-#define GEMV_COLS_ONESHOT 1
-#endif
-// one-shot shape: waves per workgroup and output rows per wave, for plain
-// columns and for the gated pair (which loads two rows per output row)
-#ifndef GEMV_COLS_OS_WAVES
-#define GEMV_COLS_OS_WAVES 8
-#endif
-#ifndef GEMV_COLS_OS_R
-#define GEMV_COLS_OS_R 2
-#endif
-#ifndef GEMV_COLS_OS_GLU_WAVES
-#define GEMV_COLS_OS_GLU_WAVES 8
-#endif
-#ifndef GEMV_COLS_OS_GLU_R
-#define GEMV_COLS_OS_GLU_R 1
-#endif
-// one-shot grid, for plain columns and for the gated pair: 0 one workgroup
-// per row tile; 1 a resident grid walking the tiles; 2 the same with the
-// tiles spread evenly over the workgroups.  Measured (graph replay): the
-// resident grid takes 2-9 % off the gated pair at 14336x4096 (8-bit at 4
-// columns 33.6 -> 30.6 us) and 0-3 % off float-format plain columns
-// (within +-1 % for the block formats).
-#ifndef GEMV_COLS_OS_PERSIST
-#define GEMV_COLS_OS_PERSIST 1
-#endif
-#ifndef GEMV_COLS_OS_PERSIST_GLU
-#define GEMV_COLS_OS_PERSIST_GLU 1
-#endif
-// f16 and the block formats take the matrix-core kernel (gemv_mfma.hip)
-// where the shape fits it
-#ifndef GEMV_COLS_MFMA
-#define GEMV_COLS_MFMA 1
-#endif
+// Launch shape (measured on MI355X, see the ColsCfg comments): 4-wave
+// workgroups for the segmented form; an x-staging budget of 64 values per
+// lane per segment and about 8 chunk loads per lane per batch; 8-wave
+// workgroups for the one-shot form, 2 output rows per wave for plain columns
+// and 1 for the gated pair (which loads a gate and an up row per output row).
+constexpr int kColsWaves = 4;
+constexpr int kColsXBudget = 64;
+constexpr int kColsLoads = 8;
+constexpr int kColsOneShotWaves = 8;
+constexpr int kColsOneShotRows = 2;
+constexpr int kColsOneShotGluWaves = 8;
+constexpr int kColsOneShotGluRows = 1;
 
-// UO == 0: segments of GEMV_COLS_X_BUDGET / (NC * E) chunks per lane.
+// UO == 0: segments of kColsXBudget / (NC * E) chunks per lane.
 // UO > 0: a whole row in one segment of UO chunks per lane ("one-shot": x of
 // every column staged once, every W chunk of the wave's rows issued at once),
 // used when that fits LDS; 8 waves of 2 rows (16 rows per workgroup) keep
 // 2 * UO loads per lane in flight.
 template <int FMT, int NC, int UO = 0, bool GLU = false> struct ColsCfg {
     static constexpr int E = Fmt<FMT>::E;
-    static constexpr int kWaves = UO > 0 ? (GLU ? GEMV_COLS_OS_GLU_WAVES : GEMV_COLS_OS_WAVES) : GEMV_COLS_WAVES;
-    // chunks per lane per segment: GEMV_COLS_X_BUDGET / (NC * E), 1..8 (a
+    static constexpr int kWaves = UO > 0 ? (GLU ? kColsOneShotGluWaves : kColsOneShotWaves) : kColsWaves;
+    // chunks per lane per segment: kColsXBudget / (NC * E), 1..8 (a
     // short segment keeps the LDS per workgroup small and occupancy up)
-    static constexpr int kU0 = GEMV_COLS_X_BUDGET / (NC * E);
+    static constexpr int kU0 = kColsXBudget / (NC * E);
     static constexpr int U = UO > 0 ? UO : (kU0 < 1 ? 1 : (kU0 > 8 ? 8 : kU0));
-    // rows per wave: about GEMV_COLS_LOADS chunk loads per lane per batch, 1..4
+    // rows per wave: about kColsLoads chunk loads per lane per batch, 1..4
     // (a gated pair loads a gate and an up row per output row: half as many)
-    static constexpr int kR0 = GEMV_COLS_LOADS / U;
-    static constexpr int kR1 = UO > 0 ? GEMV_COLS_OS_R : (kR0 > 4 ? 4 : (kR0 < 1 ? 1 : kR0));
-    static constexpr int R = GLU ? (UO > 0 ? GEMV_COLS_OS_GLU_R : (kR1 > 1 ? kR1 / 2 : 1)) : kR1;
+    static constexpr int kR0 = kColsLoads / U;
+    static constexpr int kR1 = UO > 0 ? kColsOneShotRows : (kR0 > 4 ? 4 : (kR0 < 1 ? 1 : kR0));
+    static constexpr int R = GLU ? (UO > 0 ? kColsOneShotGluRows : (kR1 > 1 ? kR1 / 2 : 1)) : kR1;
     static constexpr int SEG = 64 * U * E;     // x floats per column per segment
     static constexpr int kPlane4 = SEG / 4;    // float4 slots per plane (a multiple of 64)
     static constexpr int kBuf4 = NC * kPlane4; // float4 slots per segment buffer
@@ -197,11 +161,9 @@ __device__ __forceinline__ void consume_cols(const Batch<FMT, R, U> &b, const f3
                     t = F::dotd(dq[r], xv, acc[r][col]);
                 acc[r][col] = valid ? t : acc[r][col];
             }
-#if GEMV_COLS_SERIAL
             // one column at a time: hoisting the x reads of every column ahead
             // of the FMAs would hold U * NC * E floats in registers
             __builtin_amdgcn_sched_barrier(0);
-#endif
         }
     }
 }
@@ -509,8 +471,11 @@ template <int FMT, int NC, int UO, bool GLU = false> hipError_t launch_cols(cons
     }
     const int rows_per_tile = C::kWaves * C::R;
     int grid = (c.N + rows_per_tile - 1) / rows_per_tile;
-    constexpr int kPersist = GLU ? GEMV_COLS_OS_PERSIST_GLU : GEMV_COLS_OS_PERSIST;
-    if constexpr (UO > 0 && kPersist > 0) {
+    // the one-shot form runs on a resident grid (occupancy x CUs) whose
+    // workgroups stage x once and walk the row tiles: measured 2-9 % faster
+    // for the gated pair at 14336x4096 (8-bit at 4 columns 33.6 -> 30.6 us)
+    // and 0-3 % for float-format plain columns
+    if constexpr (UO > 0) {
         fn = reinterpret_cast<const void *>(&gemv_cols_tiles_kernel<FMT, NC, UO, GLU>);
         static std::once_flag once;
         static hipError_t attr_err = hipSuccess;
@@ -525,14 +490,8 @@ template <int FMT, int NC, int UO, bool GLU = false> hipError_t launch_cols(cons
         if (attr_err != hipSuccess)
             return attr_err;
         const int slots = (per_cu > 0 ? per_cu : 1) * device_cus();
-        if (grid > slots) {
-            if (kPersist == 2) {
-                const int per_wg = (grid + slots - 1) / slots;
-                grid = (grid + per_wg - 1) / per_wg;
-            } else {
-                grid = slots;
-            }
-        }
+        if (grid > slots)
+            grid = slots;
     }
     const unsigned char *W = c.W;
     const float *x = c.x;
@@ -588,7 +547,7 @@ template <int FMT, int NC, bool GLU = false> hipError_t dispatch_cols(const Cols
         const int64_t lds = (int64_t)NC * kWave * cpl * Fmt<FMT>::E * 4;
         const int64_t wgs = (c.N + 15) / 16, cus = device_cus();
         const bool take = Fmt<FMT>::kBlock || lds <= 64 * 1024 || (NC >= 3 && wgs == cus);
-        if (GEMV_COLS_ONESHOT && cpl <= UO && take)
+        if (cpl <= UO && take)
             return launch_cols<FMT, NC, UO, GLU>(c, s);
     }
     return launch_cols<FMT, NC, 0, GLU>(c, s);
@@ -658,7 +617,7 @@ int gemv_ncols_kernel(int wfmt, int64_t N, int64_t K, int64_t ncols)
         return GEMV_E_DIM;
     if (ncols == 1)
         return GEMV_KERNEL_ONE_COLUMN;
-    if (GEMV_COLS_MFMA && gemv::cols_mfma_plan(wfmt, (int)ncols, N, K, gemv::device_cus()).rt)
+    if (gemv::cols_mfma_plan(wfmt, (int)ncols, N, K, gemv::device_cus()).rt)
         return GEMV_KERNEL_COLUMNS_MATRIX;
     return gemv::cols_fast(wfmt, K) ? GEMV_KERNEL_COLUMNS : GEMV_KERNEL_COLUMNS_GENERIC;
 }
@@ -675,11 +634,11 @@ int gemv_fused_ncols(const void *W, int wfmt, int64_t N, int64_t K, int64_t ncol
     gemv::ColsCall c{static_cast<const unsigned char *>(W), x, (int)N, (int)K, act,
                      mul_operand ? mul_operand->data : nullptr, add_operand ? add_operand->data : nullptr,
                      dst->data};
-    if (GEMV_COLS_MFMA) {
-        const int e = gemv::launch_cols_mfma(wfmt, (int)ncols, c, hip_stream);
-        if (e >= 0)
-            return gemv::finish_launch(e);
-    }
+    // f16, bf16 and the block formats take the matrix-core kernel
+    // (gemv_mfma.hip) where the shape fits it
+    const int e = gemv::launch_cols_mfma(wfmt, (int)ncols, c, hip_stream);
+    if (e >= 0)
+        return gemv::finish_launch(e);
     return gemv::finish_launch(
         (int)gemv::dispatch_ncols(wfmt, (int)ncols, c, static_cast<hipStream_t>(hip_stream)));
 }
@@ -697,7 +656,7 @@ int gemv_glu_ncols(const void *W_gate, const void *W_up, int wfmt, int64_t N, in
     // product into dst, then the gate's with silu(g) * u in place (dst is
     // the multiplier's identical view).  apply_epilogue's SILU_MUL and
     // apply_glu's SILU are the same arithmetic.
-    if (GEMV_COLS_MFMA && act == GEMV_ACT_SILU && gemv::cols_mfma_plan(wfmt, (int)ncols, N, K, gemv::device_cus()).rt) {
+    if (act == GEMV_ACT_SILU && gemv::cols_mfma_plan(wfmt, (int)ncols, N, K, gemv::device_cus()).rt) {
         const gemv::ColsCall up{static_cast<const unsigned char *>(W_up), x, (int)N, (int)K, GEMV_ACT_NONE, nullptr,
                                 nullptr, dst->data};
         int e = gemv::launch_cols_mfma(wfmt, (int)ncols, up, hip_stream);

@@ -139,15 +139,6 @@ template <int FMT, int kStage> struct XStage {
 };
 
 
-// Optional occupancy floor (waves per SIMD) for the register allocator; 0 = none.
-#ifndef GEMV_MIN_WAVES_PER_SIMD
-#define GEMV_MIN_WAVES_PER_SIMD 0
-#endif
-template <int WAVES> constexpr int min_blocks_per_cu()
-{
-    return GEMV_MIN_WAVES_PER_SIMD > 0 ? (GEMV_MIN_WAVES_PER_SIMD * 4 + WAVES - 1) / WAVES : 1;
-}
-
 
 // ------------------------------------------------------------------ signed Hadamard prologue
 // "vulkan: fuse the sign multiply into the Hadamard FWHT", Overview: x is
@@ -293,7 +284,7 @@ struct FwhtTile {
 };
 
 template <int FMT, int WAVES, int R, int U, bool MULTI, bool GLU, bool FWHT = false>
-__global__ __launch_bounds__(WAVES *kWave, min_blocks_per_cu<WAVES>()) void gemv_fast_kernel(const unsigned char *__restrict__ W,
+__global__ __launch_bounds__(WAVES *kWave, 1) void gemv_fast_kernel(const unsigned char *__restrict__ W,
                                                                  const unsigned char *__restrict__ W2,
                                                                  const float *__restrict__ x, int N, int K,
                                                                  int act, const float *mop, const float *rop,
@@ -542,23 +533,11 @@ template <int FMT, bool GLU> hipError_t launch_generic(const Call &c, hipStream_
 
 // Waves per workgroup: float formats favour smaller workgroups (more of them
 // resident per CU), block formats larger ones (fewer copies of x staged).
-#ifndef GEMV_WAVES_FLOAT
-#define GEMV_WAVES_FLOAT 4
-#endif
-#ifndef GEMV_WAVES_BLOCK
-#define GEMV_WAVES_BLOCK 8
-#endif
-#ifndef GEMV_LOADS_PER_LANE
-#define GEMV_LOADS_PER_LANE 8
-#endif
-#ifndef GEMV_MIN_TILES
-#define GEMV_MIN_TILES 512
-#endif
-#ifndef GEMV_ADAPT_WAVES
-#define GEMV_ADAPT_WAVES 1
-#endif
-template <int FMT> constexpr int waves_of() { return Fmt<FMT>::kBlock ? GEMV_WAVES_BLOCK : GEMV_WAVES_FLOAT; }
-constexpr int kLoadsPerLane = GEMV_LOADS_PER_LANE; // R * U target
+template <int FMT> constexpr int waves_of() { return Fmt<FMT>::kBlock ? 8 : 4; }
+constexpr int kLoadsPerLane = 8; // R * U target
+// Below this many row tiles a launch takes one row per wave, so that more
+// CUs take part.
+constexpr int kMinTiles = 512;
 
 // Rows per wave for a batch of U chunk loads per row: about kLoadsPerLane
 // loads of 16 bytes per lane in flight.  A row longer than one batch (more
@@ -579,7 +558,7 @@ template <int FMT, int kWaves, int U, bool GLU, bool FWHT> hipError_t launch_uw(
     }
     // Few tiles: one row per wave so that more CUs take part.
     const int64_t tiles = ((int64_t)c.N + kWaves * R - 1) / (kWaves * R);
-    if (!FWHT && R > 1 && tiles < GEMV_MIN_TILES)
+    if (!FWHT && R > 1 && tiles < kMinTiles)
         return launch_fast<FMT, kWaves, 1, U, false, GLU, FWHT>(c, s);
     return launch_fast<FMT, kWaves, R, U, false, GLU, FWHT>(c, s);
 }
@@ -596,7 +575,7 @@ template <int FMT, int kWaves, int U, bool GLU, bool FWHT> hipError_t launch_uw(
 // chunks) is the same whatever it picks.
 template <int FMT, int U, bool GLU, bool FWHT = false> hipError_t launch_u(const Call &c, hipStream_t s, bool multi)
 {
-    if constexpr (!Fmt<FMT>::kBlock && !GLU && GEMV_ADAPT_WAVES) {
+    if constexpr (!Fmt<FMT>::kBlock && !GLU) {
         const int64_t cus = device_cus();
         if (multi && U >= 5) {
             const int cpl = (c.K / Fmt<FMT>::E + kWave - 1) / kWave;

@@ -5,14 +5,14 @@
 // state across uses must be reset, as the closing comment of "vulkan: fuse
 // the sign multiply into the Hadamard FWHT" found; this one keeps none).
 //
-// The overlap rule follows "feat(cuda): fuse activations and residual add into
-// mmv f/q epilogues", "What changed", implementation notes: the destination
-// may alias the multiply/add operand element for element (an in-place op
-// reads and writes the same index) but must not alias the matmul inputs,
-// which are read across the whole reduction; operands must be contiguous and
-// of the same shape.  The operand guards of "ggml-cpu: fuse element-wise
+// The overlap rule is the one of "feat(cuda): fuse activations and residual
+// add into mmv f/q epilogues", "What changed" (implementation notes): writing
+// output i over operand element i is safe, since each output reads only its
+// own operand element before its one store; any other overlap of dst with the
+// weights or with x is refused, because every output reads all of them.
+// Operands are contiguous and of dst's shape.  "ggml-cpu: fuse element-wise
 // epilogues (ADD, MUL, SILU) into ggml_compute_forward_mul_mat", "Guards",
-// add: f32, identically shaped (no broadcast), row-contiguous.
+// adds the operand conditions: f32, no broadcast, rows contiguous.
 #include "gemv_internal.h"
 
 #include <climits>

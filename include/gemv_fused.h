@@ -14,11 +14,11 @@
  *    quantised weights on the decode path, one destination column.
  *    "What changed": the tails sigmoid and silu, silu followed by a multiply
  *    with a per-row operand, and a residual add that may reach the product
- *    through a reshape; implementation notes: the activation is a run-time
- *    switch (with a value meaning "none"), the result is written with the
- *    matmul geometry into the final node's buffer, the destination may alias
- *    the multiply/add operand element for element but never the matmul
- *    inputs, and operands must be contiguous and of the same shape.
+ *    through a reshape; implementation notes: the activation is selected at
+ *    run time (one value meaning "none"); the output keeps the product's
+ *    element order even when the caller's buffer is a reshaped view; output i
+ *    may overwrite operand element i, nothing else may overlap the weights or
+ *    x; operands are contiguous and shaped like the output.
  *    "Why": every folded tail saves a launch, and the residual add also saves
  *    a write and a read of the output.
  *  - "ggml-cpu: fuse element-wise epilogues (ADD, MUL, SILU) into

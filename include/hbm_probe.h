@@ -38,6 +38,31 @@ int hbm_read_once_blocks(int64_t nbytes);
  * floats. */
 int hbm_read_once_store(const void *buf, int64_t nbytes, float *out, void *hip_stream);
 
+/* The read-plus-one-store-per-wave floor in other launch shapes, so that
+ * the floor a call is measured against is the best of several:
+ *   shape 0: one pass, 4-wave workgroups, 8 loads of 16 bytes per lane
+ *            (the same as hbm_read_once_store);
+ *   shape 1: one pass, 16-wave workgroups, 4 loads per lane;
+ *   shape 2: a resident grid (2 workgroups per compute unit) of 16-wave
+ *            workgroups whose waves walk the buffer 4 loads per lane at a
+ *            time.
+ * nbytes and buf as for hbm_read_once; out must hold
+ * hbm_read_floor_out_floats(nbytes, shape) floats.  Returns -1 on bad
+ * arguments (also for shape outside 0..hbm_read_floor_shapes()-1). */
+int hbm_read_floor_shapes(void);
+int64_t hbm_read_floor_out_floats(int64_t nbytes, int shape);
+int hbm_read_floor(const void *buf, int64_t nbytes, float *out, int shape, void *hip_stream);
+
+/* The one-column GEMV's arithmetic alone for an N x K call of format wfmt
+ * (a GEMV_W_* value): every row's ceil(K / E / 64) chunks per lane of 16
+ * bytes decoded and multiplied into f32 sums with the library's own decoders
+ * (E values per chunk), then reduced over the wave, one row per wave in
+ * 8-wave workgroups, on words made in registers: no weight byte is read.
+ * Its launch time is the floor the vector ALUs set for that call.  x: at
+ * least 64 floats; out: N floats (row sums of the synthetic words).
+ * Returns -1 on bad arguments. */
+int gemv_valu_floor(int wfmt, int64_t N, int64_t K, const float *x, float *out, void *hip_stream);
+
 /* dst[0..nbytes) = src[0..nbytes) with 128-bit loads and stores; nbytes a
  * positive multiple of 16, both pointers 16-byte aligned, no overlap. */
 int hbm_copy(const void *src, void *dst, int64_t nbytes, void *hip_stream);
