@@ -248,15 +248,15 @@ template <> struct Fmt<GEMV_W_Q8B32> {
                 r.w[4 * i + b] = (float)(int)(signed char)((d[i] >> (8 * b)) & 0xFF);
         return r;
     }
-    __device__ static __forceinline__ float dotd(const Dq &w, const float *xv, float scale, float acc)
+    __device__ static __forceinline__ float dotd(const Dq &w, const float *xv, _Float16 scale, float acc)
     {
         float p = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             p = fmaf(w.w[i], xv[i], p);
-        return fmaf(p, scale, acc);
+        return fmaf(p, (float)scale, acc);
     }
-    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float scale, float acc)
+    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, _Float16 scale, float acc)
     {
         unsigned d[4] = {q.x, q.y, q.z, q.w};
         float p = 0.0f;
@@ -268,7 +268,7 @@ template <> struct Fmt<GEMV_W_Q8B32> {
                 p = fmaf(w, xv[4 * i + b], p);
             }
         }
-        return fmaf(p, scale, acc);
+        return fmaf(p, (float)scale, acc);
     }
 };
 
@@ -285,34 +285,46 @@ __device__ __forceinline__ unsigned and_or(unsigned d, unsigned mask, unsigned b
 // 4-bit blocks: a chunk is one whole block of 32 codes.  A dword holds
 // elements 8i..8i+7, element k in bits 4k..4k+3.  OR-ing a nibble into the
 // mantissa of the f16 constant 1024 gives 1024 + c exactly (nibble at bit 0)
-// or 1024 + 16c (nibble at bit 4); subtracting 1032 or 1152 leaves c - 8 or
-// 16 (c - 8) exactly, as a packed f16 pair.  The 16x lane is folded back with
-// an exact multiply by 1/16 once per block.
+// or 1024 + 16c (nibble at bit 4); subtracting 1032 leaves c - 8 exactly, and
+// (1024 + 16c) / 16 - 72, one packed f16 FMA, leaves c - 8 exactly too (the
+// product is 64 + c, the sum c - 8, each exact in f16).  Each instruction
+// turns two nibbles into two exact f16 weights.  The block's sum is then
+// scaled by its fp16 scale in one mixed-precision FMA.
 template <> struct Fmt<GEMV_W_Q4B32> {
     static constexpr int E = 32, XS = 36;
     static constexpr bool kBlock = true;
     static constexpr int kChunksPerBlock = 1;
     struct Dq {
-        f16x2 h[4][4]; // per dword: (c0-8, c4-8), 16(c1-8, c5-8), (c2-8, c6-8), 16(c3-8, c7-8)
+        f16x2 h[4][4]; // per dword: (c0-8, c4-8), (c1-8, c5-8), (c2-8, c6-8), (c3-8, c7-8)
     };
+    // low nibbles of each 16-bit half: 1024 + c -> c - 8
+    __device__ static __forceinline__ f16x2 lo_pair(unsigned d)
+    {
+        const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+        return __builtin_bit_cast(f16x2, and_or(d, 0x000F000Fu, 0x64006400u)) - off;
+    }
+    // second nibbles: 1024 + 16 c -> (1024 + 16 c) / 16 - 72 = c - 8
+    __device__ static __forceinline__ f16x2 hi_pair(unsigned d)
+    {
+        const f16x2 k = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const f16x2 off = {(_Float16)-72.0f, (_Float16)-72.0f};
+        return __builtin_elementwise_fma(__builtin_bit_cast(f16x2, and_or(d, 0x00F000F0u, 0x64006400u)), k, off);
+    }
     __device__ static __forceinline__ Dq decode(u32x4 q)
     {
-        const f16x2 off1 = {(_Float16)1032.0f, (_Float16)1032.0f};
-        const f16x2 off16 = {(_Float16)1152.0f, (_Float16)1152.0f};
-        const unsigned magic = 0x64006400u;
         unsigned d[4] = {q.x, q.y, q.z, q.w};
         Dq r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const unsigned e = d[i] >> 8;
-            r.h[i][0] = __builtin_bit_cast(f16x2, and_or(d[i], 0x000F000Fu, magic)) - off1;
-            r.h[i][1] = __builtin_bit_cast(f16x2, and_or(d[i], 0x00F000F0u, magic)) - off16;
-            r.h[i][2] = __builtin_bit_cast(f16x2, and_or(e, 0x000F000Fu, magic)) - off1;
-            r.h[i][3] = __builtin_bit_cast(f16x2, and_or(e, 0x00F000F0u, magic)) - off16;
+            r.h[i][0] = lo_pair(d[i]);
+            r.h[i][1] = hi_pair(d[i]);
+            r.h[i][2] = lo_pair(e);
+            r.h[i][3] = hi_pair(e);
         }
         return r;
     }
-    __device__ static __forceinline__ float dotd(const Dq &w, const float *xv, float scale, float acc)
+    __device__ static __forceinline__ float dotd(const Dq &w, const float *xv, _Float16 scale, float acc)
     {
         float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
@@ -327,23 +339,20 @@ template <> struct Fmt<GEMV_W_Q4B32> {
             a1 = fmaf((float)w.h[i][3].x, xi[3], a1);
             a1 = fmaf((float)w.h[i][3].y, xi[7], a1);
         }
-        return fmaf(fmaf(a1, 0.0625f, a0), scale, acc);
+        return fmaf(a0 + a1, (float)scale, acc);
     }
-    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, float scale, float acc)
+    __device__ static __forceinline__ float dot(u32x4 q, const float *xv, _Float16 scale, float acc)
     {
-        const f16x2 off1 = {(_Float16)1032.0f, (_Float16)1032.0f};
-        const f16x2 off16 = {(_Float16)1152.0f, (_Float16)1152.0f};
-        const unsigned magic = 0x64006400u;
         unsigned d[4] = {q.x, q.y, q.z, q.w};
         float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float *xi = xv + 8 * i;
             const unsigned e = d[i] >> 8;
-            f16x2 h0 = __builtin_bit_cast(f16x2, and_or(d[i], 0x000F000Fu, magic)) - off1;  // c0-8, c4-8
-            f16x2 h1 = __builtin_bit_cast(f16x2, and_or(d[i], 0x00F000F0u, magic)) - off16; // 16(c1-8), 16(c5-8)
-            f16x2 h2 = __builtin_bit_cast(f16x2, and_or(e, 0x000F000Fu, magic)) - off1;     // c2-8, c6-8
-            f16x2 h3 = __builtin_bit_cast(f16x2, and_or(e, 0x00F000F0u, magic)) - off16;    // 16(c3-8), 16(c7-8)
+            const f16x2 h0 = lo_pair(d[i]); // c0-8, c4-8
+            const f16x2 h1 = hi_pair(d[i]); // c1-8, c5-8
+            const f16x2 h2 = lo_pair(e);    // c2-8, c6-8
+            const f16x2 h3 = hi_pair(e);    // c3-8, c7-8
             a0 = fmaf((float)h0.x, xi[0], a0);
             a0 = fmaf((float)h0.y, xi[4], a0);
             a0 = fmaf((float)h2.x, xi[2], a0);
@@ -353,7 +362,7 @@ template <> struct Fmt<GEMV_W_Q4B32> {
             a1 = fmaf((float)h3.x, xi[3], a1);
             a1 = fmaf((float)h3.y, xi[7], a1);
         }
-        return fmaf(fmaf(a1, 0.0625f, a0), scale, acc);
+        return fmaf(a0 + a1, (float)scale, acc);
     }
 };
 
@@ -369,9 +378,16 @@ __device__ __forceinline__ float load_scale(const unsigned char *p)
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// A block scale kept as loaded: the dot products take it as the f16 operand
+// of their final mixed-precision FMA, which converts it exactly.
+__device__ __forceinline__ _Float16 load_scale_h(const unsigned char *p)
+{
+    return __builtin_bit_cast(_Float16, *reinterpret_cast<const unsigned short *>(p));
+}
+
 template <int FMT, int R, int U> struct Batch {
     u32x4 q[R][U];
-    float sc[R][U];
+    _Float16 sc[R][U];
 };
 
 template <int FMT, int R, int U>
@@ -381,12 +397,14 @@ __device__ __forceinline__ void issue_batch(Batch<FMT, R, U> &b, const unsigned 
     using F = Fmt<FMT>;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int c = min(lane + kWave * (jb + u), nchunks - 1);
+        // non-negative and below 2^31: as an unsigned offset the load takes the
+        // row's (uniform) base address from scalar registers
+        const unsigned c = (unsigned)min(lane + kWave * (jb + u), nchunks - 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             b.q[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[r]) + c);
             if constexpr (F::kBlock)
-                b.sc[r][u] = load_scale(srow[r] + 2 * (c / F::kChunksPerBlock));
+                b.sc[r][u] = load_scale_h(srow[r] + 2 * (c / F::kChunksPerBlock));
         }
     }
 }

@@ -74,7 +74,7 @@ __device__ __forceinline__ void consume_batch(const Batch<FMT, R, U> &b, const f
     for (int u = 0; u < U; ++u) {
         const int craw = lane + kWave * (jb + u);
         const bool valid = craw < nchunks;
-        const int c = min(craw, nchunks - 1);
+        const unsigned c = (unsigned)min(craw, nchunks - 1);
         float xv[F::E];
         const f32x4 *xl = reinterpret_cast<const f32x4 *>(xs + c * F::XS);
 #pragma unroll
@@ -132,7 +132,8 @@ template <int FMT, int kStage> struct XStage {
         const int nt = blockDim.x;
 #pragma unroll
         for (int j = 0; j < kStage; ++j) {
-            const int k = 4 * min(base + j * nt + (int)threadIdx.x, K / 4 - 1);
+            // non-negative: unsigned division by the power-of-two E is a shift
+            const unsigned k = 4u * (unsigned)min(base + j * nt + (int)threadIdx.x, K / 4 - 1);
             *reinterpret_cast<f32x4 *>(xs + (k / F::E) * F::XS + (k % F::E)) = v[j];
         }
     }

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(512) void valu_floor_kernel(const float *__restrict
         const u32x4 q = {s & 0x3F7F7F7Fu, (s ^ 0x5A5A5A5Au) & 0x3F7F7F7Fu, (s + 0x12345678u) & 0x3F7F7F7Fu,
                          (s * 3u) & 0x3F7F7F7Fu};
         if constexpr (F::kBlock)
-            acc = F::dot(q, xv, 0.01f, acc);
+            acc = F::dot(q, xv, (_Float16)0.01f, acc);
         else
             acc = F::dot(q, xv, acc);
     }
