@@ -42,11 +42,12 @@ PEAK_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PEAK_MFMA_F16_TFLOPS = 2500.0
 ROTATE_MIN_BYTES = 512 << 20
 DEFAULT_WORKLOAD = "q4b32_decode_layer"
-# the device code of the one-column kernels (the kernels the counter and trace
-# summaries cover; entry points and host checks excluded): a summary stays
-# valid while these files are unchanged
+# the library's device code (every kernel a counter or trace summary can
+# cover; host checks excluded): a summary stays valid while these files are
+# unchanged
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_gemv_elementwise_amd", "csrc", f)
-                  for f in ("gemv_device.h", "gemv_fast.h")]
+                  for f in ("gemv_device.h", "gemv_fast.h", "gemv_kernels.hip", "gemv_cols.hip",
+                            "gemv_mfma.hip", "gemv_fwht.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -68,6 +69,9 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU-oracle sample length (0 disables the CPU legs)")
     p.add_argument("--no-probe", action="store_true", help="skip the bandwidth probe and the floor measurements")
+    p.add_argument("--skip-other", action="store_true",
+                   help="do not also time the opposite composition (fused vs unfused), so that a profiler's "
+                        "trace holds only the primary one's kernels")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes, 5 times (calibrates the "
                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count), then exit")
@@ -622,7 +626,7 @@ def bench_workload(torch, binding, synth, name, args, probe):
 
     # the same step with every epilogue as a separate pass (the fusion effect)
     other = None
-    if any(c.act != "none" or c.w2 or c.fwht for c in wl.calls):
+    if not args.skip_other and any(c.act != "none" or c.w2 or c.fwht for c in wl.calls):
         ostep = Step(torch, binding, wl, not args.unfused)
         osecs = time_steps(torch, ostep, args.steps, args.warmup, args.launch, args.repeats)
         other = {"us_per_step": round(float(np.median(osecs)) / args.steps * 1e6, 3),
@@ -693,8 +697,9 @@ def bench_workload(torch, binding, synth, name, args, probe):
     peak_flops = PEAK_MFMA_F16_TFLOPS if cols_kernel == "columns_matrix" else PEAK_VALU_TFLOPS
     if dom_flops / (peak_flops * 1e12) > dom_bytes / (PEAK_HBM_GBPS * 1e9):
         tflops = dom_flops / dom_sec / 1e12
-        res["roofline"].update({"bound": "alu", "achieved": round(tflops, 3), "peak": round(PEAK_VALU_TFLOPS, 1),
-                                "unit": "TFLOP/s", "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
+        res["roofline"].update({"bound": "alu" if peak_flops == PEAK_VALU_TFLOPS else "mfma",
+                                "achieved": round(tflops, 3), "peak": round(peak_flops, 1),
+                                "unit": "TFLOP/s", "frac": round(tflops / peak_flops, 4),
                                 "algorithmic_flops_per_launch": dom_flops,
                                 "hbm_gbps": round(achieved, 2)})
     if probe is not None:
