@@ -747,9 +747,11 @@ def main():
         probe, ok = probe_bandwidth(torch)
         log(f"read probe: {probe:.1f} GB/s (sum check {'ok' if ok else 'FAILED'})")
     names = list(synth.WORKLOADS) if args.workload == "all" else [args.workload]
-    for i, name in enumerate(names):
+    # the CPU legs run once: on the default workload, else on the first one
+    cpu_on = DEFAULT_WORKLOAD if DEFAULT_WORKLOAD in names else names[0]
+    for name in names:
         res, wl = bench_workload(torch, binding, synth, name, args, probe)
-        if i == 0 and args.cpu_seconds > 0:
+        if name == cpu_on and args.cpu_seconds > 0:
             log("cpu baseline (oracle, one thread, then every host thread)")
             res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
             log("cpu comparison (tile-fused GEMV, every host thread)")
