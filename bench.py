@@ -566,14 +566,18 @@ def read_counters(workload):
 
 
 def read_trace(workload):
-    """Average device duration (us) of this workload's dominant kernel from the
-    committed rocprofv3 kernel-trace summary, if it was taken on the current
-    kernel source; else None."""
+    """Average device durations (us) of this workload's dominant kernel and of
+    the best read + store floor kernel traced beside it, from the committed
+    rocprofv3 kernel-trace summary, if it was taken on the current kernel
+    source; else None for each."""
     kv = _read_summary(os.path.join(PROFILES, f"trace_{workload}.txt"))
-    try:
-        return None if kv is None else float(kv["dominant_kernel_avg_ns"]) / 1e3
-    except (KeyError, ValueError):
-        return None
+
+    def us(key):
+        try:
+            return float(kv[key].split()[0]) / 1e3
+        except (KeyError, ValueError, IndexError, TypeError):
+            return None
+    return us("dominant_kernel_avg_ns"), us("trace_read_store_floor_avg_ns")
 
 
 # ------------------------------------------------------------------ one workload
@@ -652,7 +656,7 @@ def bench_workload(torch, binding, synth, name, args, probe):
     achieved = dom_bytes / dom_sec / 1e9
     cols_kernel = binding.gemv_ncols_kernel(dom_w.fmt, dom_w.N, dom_w.K, dom.ncols) if dom.ncols > 1 else None
     traffic = read_counters(name)
-    trace_us = read_trace(name)
+    trace_us, trace_floor_us = read_trace(name)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -686,6 +690,7 @@ def bench_workload(torch, binding, synth, name, args, probe):
                      "us_per_launch": round(dom_sec * 1e6, 3),
                      "us_per_launch_min": round(min(dom_secs) * 1e6, 3),
                      "trace_us_per_launch": None if trace_us is None else round(trace_us, 3),
+                     "trace_same_size_read_store_us": None if trace_floor_us is None else round(trace_floor_us, 3),
                      "stream_us_per_call": None if stream_us is None else round(stream_us, 3)},
     }
     if other is not None:
