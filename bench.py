@@ -60,7 +60,7 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--repeats", type=int, default=7, help="timed replays of the `steps` steps (median reported)")
+    p.add_argument("--repeats", type=int, default=10, help="timed replays of the `steps` steps (median and minimum reported)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD,
                    help="a workload name, or 'all' (one JSON line each)")
     p.add_argument("--launch", choices=["graph", "stream"], default="graph")
