@@ -15,15 +15,16 @@
 //    8-bit codes and (code - 8) of the 4-bit format are exact in f16.
 //  * A (16 x 32) is x: row m = 2 b + piece of column b.  For the f16 MFMA
 //    each column is scaled by a power of two 2^(15 - e_b) (e_b the binary
-//    exponent of max_k |x_bk|) and split into hi = f16(x') and
+//    exponent of the largest finite |x_bk|) and split into hi = f16(x') and
 //    lo = f16(2^10 (x' - hi)), both rounded toward zero: every product with
 //    an f16 weight is exact in f32, hi + 2^-10 lo carries x' to 2^-20
 //    relative, and because lo is scaled up the f16 subnormals only limit
 //    values below 2^-48 of the column's largest.  For the bf16 MFMA, hi is
 //    the upper half of x and lo that of x - hi (2^-15 relative; bf16 has the
-//    exponent range of f32, so nothing is scaled).  The pieces of every
-//    column are built once per workgroup in LDS, in the A operand's lane
-//    layout.
+//    exponent range of f32, so nothing is scaled).  An infinite x is hi
+//    alone (lo = 0) and a NaN x a NaN piece, so special values propagate as
+//    in the plain product.  The pieces of every column are built once per
+//    workgroup in LDS, in the A operand's lane layout.
 //  * D (16 x 16): lane n + 16 g' holds row n of pieces 4 g' .. 4 g' + 3, that
 //    is hi and lo of columns 2 g' and 2 g' + 1, so a column is finished
 //    without lane exchange: y = (hi + 2^-10 lo) 2^(e_b - 15) (hi + lo for
@@ -78,6 +79,14 @@ __device__ __forceinline__ float wave_max(float v)
     v = fmaxf(v, dpp<0x141>(v));
     v = fmaxf(v, dpp<0x140>(v));
     return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
+}
+
+// |v| where v is finite, else 0: a column's scale exponent comes from its
+// largest finite magnitude (infinities and NaNs are carried as themselves).
+__device__ __forceinline__ float finite_abs(float v)
+{
+    const float a = fabsf(v);
+    return a <= 3.40282347e38f ? a : 0.0f;
 }
 
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 q) { return __builtin_bit_cast(f16x8, q); }
@@ -199,22 +208,33 @@ __host__ __device__ inline int mfma_spw(int nsteps, int KS, bool block)
 // The hi and lo pieces of one octet of x (v, in position order) into their
 // A-layout slots: slot[0] (hi) and slot[rs] (lo).  sh: the column's scale
 // exponent (unused for bf16, whose pieces are not scaled).
+//
+// Special values keep IEEE semantics: an infinite x is carried whole by hi
+// (an infinity of f16 or bf16) with lo = 0, so that the matrix core forms
+// w * inf (and 0 * inf = NaN) as the plain product would; a NaN x gives a
+// NaN piece.  The column's scale exponent comes from its largest finite
+// magnitude (finite_abs).
 template <int FMT> __device__ __forceinline__ void write_pieces(const float (&v)[8], int sh, u32x4 *slot, int rs)
 {
     unsigned hw[4], lw[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
         if constexpr (FMT == GEMV_W_BF16) {
+            // the upper half of an infinity is the bf16 infinity itself
             const unsigned b0 = __builtin_bit_cast(unsigned, v[e]), b1 = __builtin_bit_cast(unsigned, v[e + 1]);
-            const float r0 = v[e] - __builtin_bit_cast(float, b0 & 0xFFFF0000u);
-            const float r1 = v[e + 1] - __builtin_bit_cast(float, b1 & 0xFFFF0000u);
+            const float r0 = __builtin_isinf(v[e]) ? 0.0f : v[e] - __builtin_bit_cast(float, b0 & 0xFFFF0000u);
+            const float r1 = __builtin_isinf(v[e + 1]) ? 0.0f : v[e + 1] - __builtin_bit_cast(float, b1 & 0xFFFF0000u);
             hw[e / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
             lw[e / 2] = __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, r1), __builtin_bit_cast(unsigned, r0), 0x07060302u);
         } else {
             const float v0 = v[slot_pos<FMT>(e)], v1 = v[slot_pos<FMT>(e + 1)];
-            const f16x2 hp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ldexpf(v0, sh), ldexpf(v1, sh)));
-            const float r0 = fmaf((float)hp.x, -1024.0f, ldexpf(v0, sh + kLoShift));
-            const float r1 = fmaf((float)hp.y, -1024.0f, ldexpf(v1, sh + kLoShift));
+            f16x2 hp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ldexpf(v0, sh), ldexpf(v1, sh)));
+            // converting an infinity to f16 gives the f16 infinity in any rounding mode
+            const bool i0 = __builtin_isinf(v0), i1 = __builtin_isinf(v1);
+            hp.x = i0 ? (_Float16)v0 : hp.x;
+            hp.y = i1 ? (_Float16)v1 : hp.y;
+            const float r0 = i0 ? 0.0f : fmaf((float)hp.x, -1024.0f, ldexpf(v0, sh + kLoShift));
+            const float r1 = i1 ? 0.0f : fmaf((float)hp.y, -1024.0f, ldexpf(v1, sh + kLoShift));
             hw[e / 2] = __builtin_bit_cast(unsigned, hp);
             lw[e / 2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(r0, r1));
         }
@@ -373,7 +393,7 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
             const bool ok = lane + kWave * i < nocts;
 #pragma unroll
             for (int p = 0; p < 8; ++p)
-                mx = fmaxf(mx, ok ? fabsf(xv[i][p]) : 0.0f);
+                mx = fmaxf(mx, ok ? finite_abs(xv[i][p]) : 0.0f);
         }
         mx = wave_max(mx);
         int ec;
@@ -511,7 +531,7 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_seg_kernel(const un
                 const bool ok = lane + kWave * i < nocts;
 #pragma unroll
                 for (int p = 0; p < 8; ++p)
-                    mx = fmaxf(mx, ok ? fabsf(xv[i][p]) : 0.0f);
+                    mx = fmaxf(mx, ok ? finite_abs(xv[i][p]) : 0.0f);
             }
             mx = wave_max(mx);
             int ec;

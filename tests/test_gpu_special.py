@@ -4,17 +4,20 @@ NaN block scale) must poison exactly its row, and an infinite x_j must give
 NaN in every row whose weight at j is exactly zero (0 * inf) and an infinity
 of the weight's sign in every other row.  The epilogues then map +inf, -inf
 and NaN accumulators as the oracle's do (sigmoid: 1, 0, NaN; silu: +inf, NaN,
-NaN).  The matrix-core column kernels are not covered: they scale each column
-of x by a power of two taken from its largest magnitude, which an infinite or
-NaN x leaves undefined."""
+NaN).  The same holds over several destination columns, on the vector-ALU
+column kernels and on the matrix-core ones (whose x pieces carry an infinity
+whole and scale each column by its largest finite magnitude)."""
+import zlib
+
 import numpy as np
 import pytest
 
 torch = pytest.importorskip("torch")
 
 import oracle
-from decode_gemv_elementwise_amd import synth
-from gpu_util import host, log, run_fused
+from oracle.compare import TOLERANCE, compare
+from decode_gemv_elementwise_amd import binding, synth
+from gpu_util import host, log, run_fused, run_ncols
 
 pytestmark = pytest.mark.gpu
 
@@ -91,3 +94,76 @@ def test_infinite_x_follows_ieee(fmt, act):
     fin = np.isfinite(y)
     if fin.any():  # sigmoid of -inf is 0, of +inf is 1: exact
         assert np.array_equal(g[fin], y[fin].astype(np.float32)), f"{fmt} {act}"
+
+
+# (format, N, K, columns, kernel the call takes): the matrix-core kernels in
+# one segment and segmented, and the vector-ALU column kernels
+COLUMN_SHAPES = [
+    ("f16", 300, 4096, 8, "columns_matrix"), ("bf16", 300, 4096, 6, "columns_matrix"),
+    ("q4b32", 300, 4096, 7, "columns_matrix"), ("q8b32", 4096, 6144, 4, "columns_matrix"),
+    ("q4b32", 67, 14336, 8, "columns_matrix"), ("f16", 67, 14336, 7, "columns_matrix"),
+    ("f16", 4096, 4096, 4, "columns"), ("bf16", 4096, 4096, 4, "columns"), ("q8b32", 4096, 4096, 4, "columns"),
+    ("q4b32", 4096, 4096, 2, "columns"), ("q4b32", 33, 96, 8, "columns"), ("f32", 4096, 4096, 8, "columns"),
+]
+
+
+def _finite_columns_within_tolerance(w, X, act, g, Y, acc, absacc, R, cols, tag):
+    for b in cols:
+        res = compare(g[b], Y[b], acc[b], absacc[b], act, r=None if R is None else R[b])
+        assert res["max_err"] <= TOLERANCE[w.fmt], f"{tag} column {b}: {res}"
+
+
+@pytest.mark.parametrize("fmt,N,K,B,kernel", COLUMN_SHAPES)
+def test_columns_infinite_and_nan_x_follow_ieee(fmt, N, K, B, kernel):
+    """Column 0 holds +inf at position j, column 1 -inf there beside a large
+    finite value, column 2 a NaN, column 3 +inf and -inf side by side; W is
+    zero at (row, j) for three rows.  Every column's NaN / infinity pattern
+    and signs match the oracle's IEEE double arithmetic, and the remaining
+    (finite) columns are unaffected."""
+    assert binding.gemv_ncols_kernel(fmt, N, K, B) == kernel
+    log(f"special: columns {fmt} {N}x{K} ncols={B} ({kernel})")
+    rng = np.random.default_rng(zlib.crc32(f"special-cols/{fmt}/{N}/{K}/{B}".encode()))
+    w = synth.random_weights(rng, fmt, N, K)
+    j = K // 3 - 5
+    zero_rows = [i for i in (3, 17, 40) if i < N]
+    for i in zero_rows:
+        _set_weight(w, i, j, "zero")
+    X = synth.draw_vec(rng, B * K).reshape(B, K)
+    X[0, j] = np.inf
+    X[1, j] = -np.inf
+    X[1, j + 7] = 1e30
+    if B > 2:
+        X[2, j + 1] = np.nan
+    if B > 3:
+        X[3, j] = np.inf
+        X[3, j + 2] = -np.inf
+    R = synth.draw_vec(rng, B * N).reshape(B, N)
+    g = run_ncols(w, X, "add", R=R).reshape(B, N)
+    Y, acc, absacc = oracle.ncols_reference(fmt, N, K, w.data, X, "add", R=R)
+    Y = np.asarray(Y)
+    for i in zero_rows:
+        assert np.isnan(Y[0, i]) and np.isnan(Y[1, i])
+    for b in range(min(B, 4)):
+        _same_pattern(g[b], Y[b], f"{fmt} {kernel} column {b}")
+    _finite_columns_within_tolerance(w, X, "add", g, Y, acc, absacc, R, range(4, B), f"{fmt} {kernel}")
+
+
+@pytest.mark.parametrize("fmt,N,K,B,kernel", COLUMN_SHAPES)
+def test_columns_nan_weight_poisons_only_its_row(fmt, N, K, B, kernel):
+    """A NaN weight (a NaN block scale for the block formats) makes its row
+    NaN in every column and leaves every other row as the oracle has it."""
+    assert binding.gemv_ncols_kernel(fmt, N, K, B) == kernel
+    log(f"special: columns NaN weight {fmt} {N}x{K} ncols={B} ({kernel})")
+    rng = np.random.default_rng(zlib.crc32(f"special-cols-w/{fmt}/{N}/{K}/{B}".encode()))
+    w = synth.random_weights(rng, fmt, N, K)
+    _set_weight(w, 5, 37, "nan")
+    X = synth.draw_vec(rng, B * K).reshape(B, K)
+    g = run_ncols(w, X, "silu").reshape(B, N)
+    Y, acc, absacc = oracle.ncols_reference(fmt, N, K, w.data, X, "silu")
+    Y = np.asarray(Y)
+    assert np.isnan(g[:, 5]).all() and np.isnan(Y[:, 5]).all()
+    rest = np.arange(N) != 5
+    assert np.isfinite(g[:, rest]).all() and np.isfinite(Y[:, rest]).all()
+    for b in range(B):
+        res = compare(g[b, rest], Y[b, rest], acc[b, rest], absacc[b, rest], "silu")
+        assert res["max_err"] <= TOLERANCE[fmt], f"{fmt} {kernel} column {b}: {res}"
