@@ -6,7 +6,8 @@ of the weight's sign in every other row.  The epilogues then map +inf, -inf
 and NaN accumulators as the oracle's do (sigmoid: 1, 0, NaN; silu: +inf, NaN,
 NaN).  The same holds over several destination columns, on the vector-ALU
 column kernels and on the matrix-core ones (whose x pieces carry an infinity
-whole and scale each column by its largest finite magnitude)."""
+whole and scale each column by its largest finite magnitude), for the gated
+pair on each of its routes, and through the signed Hadamard prologue."""
 import zlib
 
 import numpy as np
@@ -15,7 +16,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle
-from oracle.compare import TOLERANCE, compare
+from oracle.compare import TOLERANCE, compare, compare_glu
 from decode_gemv_elementwise_amd import binding, synth
 from gpu_util import host, log, run_fused, run_ncols
 
@@ -167,3 +168,81 @@ def test_columns_nan_weight_poisons_only_its_row(fmt, N, K, B, kernel):
     for b in range(B):
         res = compare(g[b, rest], Y[b, rest], acc[b, rest], absacc[b, rest], "silu")
         assert res["max_err"] <= TOLERANCE[fmt], f"{fmt} {kernel} column {b}: {res}"
+
+
+def _run_glu(wg, wu, X, act):
+    """gemv_glu (X of one row) or gemv_glu_ncols; the float32 output [B, N]."""
+    B = X.shape[0]
+    Wg, Wu = torch.from_numpy(wg.data).cuda(), torch.from_numpy(wu.data).cuda()
+    Xd = torch.from_numpy(np.ascontiguousarray(X.reshape(-1) if B == 1 else X)).cuda()
+    dst = torch.full((B, wg.N) if B > 1 else (wg.N,), float("nan"), dtype=torch.float32, device="cuda")
+    if B == 1:
+        binding.gemv_glu(Wg, Wu, wg.fmt, wg.N, wg.K, Xd, act, dst=dst)
+    else:
+        binding.gemv_glu_ncols(Wg, Wu, wg.fmt, wg.N, wg.K, B, Xd, act, dst=dst)
+    torch.cuda.synchronize()
+    return host(dst).reshape(B, wg.N)
+
+
+# (format, N, K, columns): one column, the one-launch pair over columns, and
+# (silu on a shape whose columns run on the matrix cores) the two matrix-core
+# launches
+GLU_SHAPES = [("q4b32", 256, 4096, 1), ("bf16", 256, 4096, 1), ("q4b32", 4096, 4096, 2), ("f16", 300, 4096, 8),
+              ("q8b32", 4096, 6144, 4)]
+
+
+@pytest.mark.parametrize("fmt,N,K,B", GLU_SHAPES)
+@pytest.mark.parametrize("act", ["silu", "sigmoid"])
+def test_gated_pair_special_values_follow_ieee(fmt, N, K, B, act):
+    """The gated pair with +inf (column 0), -inf (column 1) and NaN (column
+    2) in x and zero gate or up weights at the infinite position in a few
+    rows: NaN / infinity patterns and signs as in the oracle's act(g) * u."""
+    log(f"special: gated pair {fmt} {N}x{K} ncols={B} {act}")
+    rng = np.random.default_rng(zlib.crc32(f"special-glu/{fmt}/{N}/{K}/{B}/{act}".encode()))
+    wg = synth.random_weights(rng, fmt, N, K)
+    wu = synth.random_weights(rng, fmt, N, K)
+    j = K // 2 + 3
+    for i in (2, 9):
+        _set_weight(wg, i, j, "zero")
+    for i in (9, 30):
+        _set_weight(wu, i, j, "zero")
+    X = synth.draw_vec(rng, B * K).reshape(B, K)
+    X[0, j] = np.inf
+    if B > 1:
+        X[1, j] = -np.inf
+    if B > 2:
+        X[2, j + 1] = np.nan
+    g = _run_glu(wg, wu, X, act)
+    for b in range(B):
+        Y, G, AG, U, AU = (np.asarray(a) for a in oracle.glu_reference(fmt, N, K, wg.data, wu.data, X[b], act))
+        if b < 3:  # a special value in this column: every row is +-inf or NaN
+            _same_pattern(g[b], Y, f"{fmt} {act} column {b}")
+            assert not np.isfinite(Y).any()
+        else:      # the other columns are untouched
+            res = compare_glu(g[b], Y, act, G, AG, U, AU)
+            assert res["max_err"] <= TOLERANCE[fmt], f"{fmt} {act} column {b}: {res}"
+
+
+@pytest.mark.parametrize("fmt", ["f16", "q4b32"])
+def test_hadamard_prologue_special_values_follow_ieee(fmt):
+    """An infinite x through the fused signed transform: its 1024-block
+    becomes infinities of the transform's signs (one infinity meets only
+    finite values in the butterflies), then the product; a NaN x poisons its
+    block.  NaN / infinity patterns and signs as in the oracle."""
+    log(f"special: signed FWHT prologue {fmt}")
+    N, K, n = 96, 2048, 1024
+    rng = np.random.default_rng(zlib.crc32(f"special-fwht/{fmt}".encode()))
+    w = synth.random_weights(rng, fmt, N, K)
+    s = np.where(rng.random(K) < 0.5, -1.0, 1.0).astype(np.float32)
+    for x_special in (np.inf, np.nan):
+        x = synth.draw_vec(rng, K)
+        x[300] = x_special
+        r = synth.draw_vec(rng, N)
+        dst = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        binding.gemv_fused_fwht(torch.from_numpy(w.data).cuda(), fmt, N, K, torch.from_numpy(x).cuda(),
+                                torch.from_numpy(s).cuda(), n, K, "add", add_operand=torch.from_numpy(r).cuda(), dst=dst)
+        torch.cuda.synchronize()
+        g = host(dst)
+        y = np.asarray(oracle.fwht_gemv_reference(fmt, N, K, w.data, x, s, n, "add", r=r)[0])
+        _same_pattern(g, y, f"{fmt} FWHT x={x_special}")
+        assert not np.isfinite(y).any()
