@@ -81,12 +81,39 @@ __device__ __forceinline__ float wave_max(float v)
     return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
 }
 
-// |v| where v is finite, else 0: a column's scale exponent comes from its
-// largest finite magnitude (infinities and NaNs are carried as themselves).
-__device__ __forceinline__ float finite_abs(float v)
+// A column's largest finite magnitude over the VO octets of x a builder
+// lane holds (octets past nocts excluded), reduced over the wave, and
+// whether the column holds an infinity.  NaNs drop out of the maximum by
+// themselves (fmaxf returns the other operand); an infinity would make the
+// scale exponent meaningless, so such a column takes a second pass over its
+// finite values.  The result is uniform across the wave.
+template <int VO>
+__device__ __forceinline__ float column_max(const float (&xv)[VO][8], int lane, int nocts, bool &has_inf)
 {
-    const float a = fabsf(v);
-    return a <= 3.40282347e38f ? a : 0.0f;
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VO; ++i) {
+        const bool ok = lane + kWave * i < nocts;
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            mx = fmaxf(mx, ok ? fabsf(xv[i][p]) : 0.0f);
+    }
+    mx = wave_max(mx);
+    has_inf = !(mx <= 3.40282347e38f);
+    if (has_inf) {
+        mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VO; ++i) {
+            const bool ok = lane + kWave * i < nocts;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const float a = fabsf(xv[i][p]);
+                mx = fmaxf(mx, ok && a <= 3.40282347e38f ? a : 0.0f);
+            }
+        }
+        mx = wave_max(mx);
+    }
+    return mx;
 }
 
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 q) { return __builtin_bit_cast(f16x8, q); }
@@ -212,9 +239,12 @@ __host__ __device__ inline int mfma_spw(int nsteps, int KS, bool block)
 // Special values keep IEEE semantics: an infinite x is carried whole by hi
 // (an infinity of f16 or bf16) with lo = 0, so that the matrix core forms
 // w * inf (and 0 * inf = NaN) as the plain product would; a NaN x gives a
-// NaN piece.  The column's scale exponent comes from its largest finite
-// magnitude (finite_abs).
-template <int FMT> __device__ __forceinline__ void write_pieces(const float (&v)[8], int sh, u32x4 *slot, int rs)
+// NaN piece (through the plain conversions already).  The column's scale
+// exponent comes from its largest finite magnitude (column_max).  For
+// the f16 pieces INF selects that care: columns without an infinity (the
+// builders know from the column's maximum) skip it.
+template <int FMT, bool INF = true>
+__device__ __forceinline__ void write_pieces(const float (&v)[8], int sh, u32x4 *slot, int rs)
 {
     unsigned hw[4], lw[4];
 #pragma unroll
@@ -230,7 +260,7 @@ template <int FMT> __device__ __forceinline__ void write_pieces(const float (&v)
             const float v0 = v[slot_pos<FMT>(e)], v1 = v[slot_pos<FMT>(e + 1)];
             f16x2 hp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(ldexpf(v0, sh), ldexpf(v1, sh)));
             // converting an infinity to f16 gives the f16 infinity in any rounding mode
-            const bool i0 = __builtin_isinf(v0), i1 = __builtin_isinf(v1);
+            const bool i0 = INF && __builtin_isinf(v0), i1 = INF && __builtin_isinf(v1);
             hp.x = i0 ? (_Float16)v0 : hp.x;
             hp.y = i1 ? (_Float16)v1 : hp.y;
             const float r0 = i0 ? 0.0f : fmaf((float)hp.x, -1024.0f, ldexpf(v0, sh + kLoShift));
@@ -387,15 +417,8 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
         // builders: column maximum -> binary exponent, then hi / lo pieces
         // of this builder's share of the column into the A layout (octet
         // o is step o / 4, lane group o % 4)
-        float mx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VO; ++i) {
-            const bool ok = lane + kWave * i < nocts;
-#pragma unroll
-            for (int p = 0; p < 8; ++p)
-                mx = fmaxf(mx, ok ? finite_abs(xv[i][p]) : 0.0f);
-        }
-        mx = wave_max(mx);
+        bool has_inf;
+        const float mx = column_max<VO>(xv, lane, nocts, has_inf);
         int ec;
         (void)frexpf(mx, &ec);
         const int sh = kXShift - ec;
@@ -406,8 +429,13 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_kernel(const unsign
 #pragma unroll
         for (int i = 0; i < VO; ++i) {
             const int o = (lane + kWave * i + rot) % nocts;
-            if (lane + kWave * i < nocts && o >= oa && o < ob)
-                write_pieces<FMT>(xv[i], sh, reinterpret_cast<u32x4 *>(lds) + 2 * c * rs + o, rs);
+            if (lane + kWave * i < nocts && o >= oa && o < ob) {
+                u32x4 *slot = reinterpret_cast<u32x4 *>(lds) + 2 * c * rs + o;
+                if (has_inf)
+                    write_pieces<FMT, true>(xv[i], sh, slot, rs);
+                else
+                    write_pieces<FMT, false>(xv[i], sh, slot, rs);
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -524,16 +552,9 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_seg_kernel(const un
     };
     auto build = [&](const float (&xv)[VO][8], int pb) {
         int sh = 0;
+        bool has_inf = true; // bf16 pieces always take the care (they have no maximum)
         if constexpr (FMT != GEMV_W_BF16) {
-            float mx = 0.0f;
-#pragma unroll
-            for (int i = 0; i < VO; ++i) {
-                const bool ok = lane + kWave * i < nocts;
-#pragma unroll
-                for (int p = 0; p < 8; ++p)
-                    mx = fmaxf(mx, ok ? finite_abs(xv[i][p]) : 0.0f);
-            }
-            mx = wave_max(mx);
+            const float mx = column_max<VO>(xv, lane, nocts, has_inf);
             int ec;
             (void)frexpf(mx, &ec);
             sh = kXShift - ec;
@@ -545,8 +566,13 @@ __global__ __launch_bounds__(kWG *kWave) void gemv_cols_mfma_seg_kernel(const un
 #pragma unroll
         for (int i = 0; i < VO; ++i) {
             const int o = (lane + kWave * i + rot) % nocts;
-            if (lane + kWave * i < nocts && o >= oa && o < ob)
-                write_pieces<FMT>(xv[i], sh, reinterpret_cast<u32x4 *>(lds + pb * bufb) + 2 * c * rs + o, rs);
+            if (lane + kWave * i < nocts && o >= oa && o < ob) {
+                u32x4 *slot = reinterpret_cast<u32x4 *>(lds + pb * bufb) + 2 * c * rs + o;
+                if (has_inf)
+                    write_pieces<FMT, true>(xv[i], sh, slot, rs);
+                else
+                    write_pieces<FMT, false>(xv[i], sh, slot, rs);
+            }
         }
     };
 
