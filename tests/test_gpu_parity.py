@@ -90,10 +90,15 @@ def test_format_epilogue_matrix(fmt, act):
 
 # ------------------------------------------------------------------ odd, ragged and extreme shapes
 
+# The largest K whose staged x fits the 160 KiB of LDS a workgroup may take,
+# and the next one (the generic kernel): f32 40960 / 40964, f16 and bf16
+# 27304 / 27312 (12 floats of LDS per 8 values), 8-bit 32768 / 32800, 4-bit
+# 36384 / 36416.
 FLOAT_SHAPES = [(1, 1), (1, 7), (3, 64), (5, 4), (33, 257), (64, 1000), (17, 4097), (4097, 33),
-                (1000, 256), (1003, 4096), (300, 8192), (67, 14336), (2, 40960), (2, 40964), (65539, 8)]
-BLOCK_SHAPES = [(1, 32), (7, 64), (33, 96), (1000, 4096), (3, 32000), (2, 36384), (2, 36416), (1, 65536),
-                (4099, 32)]
+                (1000, 256), (1003, 4096), (300, 8192), (67, 14336), (2, 27304), (2, 27312), (2, 40960),
+                (2, 40964), (65539, 8)]
+BLOCK_SHAPES = [(1, 32), (7, 64), (33, 96), (1000, 4096), (3, 32000), (2, 32768), (2, 32800), (2, 36384),
+                (2, 36416), (1, 65536), (4099, 32)]
 
 
 @pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
