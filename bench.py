@@ -90,6 +90,8 @@ def probe_lib():
     lib.hbm_read_floor_out_floats.restype = i64
     lib.hbm_read_floor_shapes.restype = ctypes.c_int
     lib.gemv_valu_floor.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
+    lib.hbm_read_once.argtypes = [vp, i64, vp, vp]
+    lib.hbm_read_once_blocks.argtypes = [i64]
     return lib
 
 
@@ -363,16 +365,44 @@ def read_floor_us(torch, nbytes, n):
              1: "one pass, 16-wave workgroups, 4 loads per lane",
              2: "resident grid, 16-wave workgroups, 4 loads per lane per step"}
     for shape in range(lib.hbm_read_floor_shapes()):
-        out = torch.zeros(int(lib.hbm_read_floor_out_floats(nbytes, shape)), dtype=torch.float32, device="cuda")
+        # the results rotate with the inputs, as a GEMV's dst does (a launch
+        # that stores over the previous launch's lines pays for it)
+        nout = int(lib.hbm_read_floor_out_floats(nbytes, shape))
+        oslot = (nout + 63) // 64 * 64
+        out = torch.zeros(copies * oslot, dtype=torch.float32, device="cuda")
 
-        def one(i, s, shape=shape, out=out):
-            rc = lib.hbm_read_floor(buf.data_ptr() + (i % copies) * slot, nbytes, out.data_ptr(), shape, s)
+        def one(i, s, shape=shape, out=out, oslot=oslot):
+            rc = lib.hbm_read_floor(buf.data_ptr() + (i % copies) * slot, nbytes,
+                                    out.data_ptr() + 4 * (i % copies) * oslot, shape, s)
             assert rc == 0, rc
         res[names.get(shape, str(shape))] = round(replay_us(torch, one, n), 3)
         del out
     del buf
     torch.cuda.empty_cache()
     return res
+
+
+def read_only_us(torch, nbytes, n):
+    """Per-launch time of merely reading nbytes in one pass (4-wave
+    workgroups, 8 loads per lane), with no store a launch must wait for, over
+    the same rotating buffers and graph replay: what the store of the read +
+    store floor adds is the difference."""
+    lib = probe_lib()
+    nbytes = (nbytes + 15) // 16 * 16
+    slot = (nbytes + 4095) // 4096 * 4096
+    copies = max(2, -(-(512 << 20) // slot))
+    buf = torch.ones(copies * slot // 4, dtype=torch.float32, device="cuda")
+    nout = int(lib.hbm_read_once_blocks(nbytes))
+    oslot = (nout + 63) // 64 * 64
+    out = torch.zeros(copies * oslot, dtype=torch.float32, device="cuda")
+
+    def one(i, s):
+        assert lib.hbm_read_once(buf.data_ptr() + (i % copies) * slot, nbytes,
+                                 out.data_ptr() + 4 * (i % copies) * oslot, s) == 0
+    us = round(replay_us(torch, one, n), 3)
+    del buf, out
+    torch.cuda.empty_cache()
+    return us
 
 
 def valu_floor_us(torch, fmt, N, K, n):
@@ -719,6 +749,7 @@ def bench_workload(torch, binding, synth, name, args, probe):
         res["roofline"]["same_size_read_store_by_shape_us"] = floors
         res["roofline"]["frac_of_same_size_read_store"] = round(floor_us / (dom_sec * 1e6), 4)
         res["roofline"]["frac_of_peak_at_floor"] = round(dom_bytes / (floor_us * 1e3) / PEAK_HBM_GBPS, 4)
+        res["roofline"]["same_size_read_only_us"] = read_only_us(torch, dom_bytes, max(50, min(args.steps, 400)))
         if dom.ncols == 1 and not dom.w2 and not dom.fwht:
             # the kernel's arithmetic alone, no weight byte read
             res["roofline"]["valu_floor_us"] = valu_floor_us(torch, dom_w.fmt, dom_w.N, dom_w.K,
