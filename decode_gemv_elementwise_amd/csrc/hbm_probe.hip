@@ -58,32 +58,6 @@ __global__ __launch_bounds__(256) void read_once_kernel(const u32x4 *__restrict_
         out[blockIdx.x] = s;
 }
 
-// The same one-pass read, then what every GEMV ends with: one 4-byte store
-// per wave (the wave's sum, reduced over its lanes so that every lane's loads
-// are used), to out[wave].  A launch ends only when its stores are
-// acknowledged, so this is the floor for a kernel that reads the bytes and
-// writes one result per wave.
-__global__ __launch_bounds__(256) void read_once_store_kernel(const u32x4 *__restrict__ a, int64_t n16, float *out)
-{
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t base = wave * 64 * kOnceLoads;
-    u32x4 v[kOnceLoads];
-#pragma unroll
-    for (int u = 0; u < kOnceLoads; ++u) {
-        const int64_t i = base + lane + 64 * u;
-        v[u] = __builtin_nontemporal_load(a + (i < n16 ? i : n16 - 1));
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kOnceLoads; ++u)
-        s += __builtin_bit_cast(float, v[u].x) + __builtin_bit_cast(float, v[u].w);
-    for (int o = 32; o > 0; o >>= 1)
-        s += __shfl_xor(s, o);
-    if (lane == 0)
-        out[wave] = s;
-}
-
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ a, u32x4 *__restrict__ b, int64_t n16)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -240,19 +214,6 @@ int hbm_read_once(const void *buf, int64_t nbytes, float *out, void *hip_stream)
     void *args[] = {&a, &n16, &out};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&read_once_kernel), dim3(hbm_read_once_blocks(nbytes)),
                                    dim3(256), args, 0, static_cast<hipStream_t>(hip_stream));
-    return e == hipSuccess ? 0 : (int)e;
-}
-
-int hbm_read_once_store(const void *buf, int64_t nbytes, float *out, void *hip_stream)
-{
-    if (!buf || !out || nbytes <= 0 || nbytes % 16 || !ok16(buf) || nbytes > (int64_t(1) << 40))
-        return -1;
-    int64_t n16 = nbytes / 16;
-    const u32x4 *a = static_cast<const u32x4 *>(buf);
-    void *args[] = {&a, &n16, &out};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&read_once_store_kernel),
-                                   dim3(hbm_read_once_blocks(nbytes)), dim3(256), args, 0,
-                                   static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? 0 : (int)e;
 }
 

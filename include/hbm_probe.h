@@ -34,14 +34,9 @@ int hbm_read_once_blocks(int64_t nbytes);
 /* The same read, then one 4-byte store per wave (its sum, reduced over its
  * lanes) to out[wave]: a launch ends only when its stores are acknowledged,
  * so this is the floor for a kernel that reads nbytes and writes a result
- * per wave, as a GEMV does.  out must hold 4 * hbm_read_once_blocks(nbytes)
- * floats. */
-int hbm_read_once_store(const void *buf, int64_t nbytes, float *out, void *hip_stream);
-
-/* The read-plus-one-store-per-wave floor in other launch shapes, so that
- * the floor a call is measured against is the best of several:
- *   shape 0: one pass, 4-wave workgroups, 8 loads of 16 bytes per lane
- *            (the same as hbm_read_once_store);
+ * per wave, as a GEMV does.  Several launch shapes, so that the floor a call
+ * is measured against is the best of them:
+ *   shape 0: one pass, 4-wave workgroups, 8 loads of 16 bytes per lane;
  *   shape 1: one pass, 16-wave workgroups, 4 loads per lane;
  *   shape 2: a resident grid (2 workgroups per compute unit) of 16-wave
  *            workgroups whose waves walk the buffer 4 loads per lane at a

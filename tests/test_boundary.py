@@ -40,8 +40,9 @@ def test_probe_library_exports_every_declared_function():
     from decode_gemv_elementwise_amd import build as bld
     text = open(os.path.join(ROOT, "include", "hbm_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = sorted(set(re.findall(r"\b(hbm_[a-z_]+)\s*\(", text)))
-    assert {"hbm_read_probe", "hbm_read_once", "hbm_read_once_blocks", "hbm_read_once_store", "hbm_copy"} <= set(names)
+    names = sorted(set(re.findall(r"\b((?:hbm|gemv)_[a-z_]+)\s*\(", text)))
+    assert {"hbm_read_probe", "hbm_read_once", "hbm_read_once_blocks", "hbm_read_floor", "hbm_read_floor_shapes",
+            "hbm_read_floor_out_floats", "gemv_valu_floor", "hbm_copy"} <= set(names)
     lib = ctypes.CDLL(bld.PROBE_LIB)
     for n in names:
         assert hasattr(lib, n), n
