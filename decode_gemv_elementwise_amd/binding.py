@@ -50,6 +50,14 @@ def load(path=None):
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -m decode_gemv_elementwise_amd.build` "
                           "(or __graft_entry__.build()) first")
+    # The library needs libamdhip64.so.7 and binds to whichever copy the
+    # process maps first; torch ships its own.  Importing torch first makes
+    # the library and torch share torch's HIP runtime (one runtime per
+    # process, the configuration every test runs in).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     lib.gemv_fused.argtypes = [_VP, ctypes.c_int, _I64, _I64, _VP, ctypes.c_int, _VIEWP, _VIEWP, _VIEWP, _VP]
     lib.gemv_fused.restype = ctypes.c_int
